@@ -1,0 +1,181 @@
+/*
+ * ikbo.h -- C ABI of the IKBO hot path for MI355X (gfx950).
+ *
+ * In-Kernel Broadcast Optimization, from ROCS (Request-Oriented Compute Sharing,
+ * arXiv 2607.27744): request-side tensors stay at their natural batch size B_r = num_req,
+ * candidate-side tensors at B_c = num_cand, and an index map m in {0..B_r-1}^{B_c} ties each
+ * candidate to its request (Sec. 4, opening paragraph; Sec. 4.1). The request-to-candidate
+ * broadcast is resolved inside the consuming kernels and is never materialised in memory.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers to tensors are DEVICE pointers unless a comment says "host". Tensors are dense,
+ *    row-major and contiguous; base pointers must be 16-byte aligned (IKBO_MISALIGNED).
+ *  - Ownership: the caller owns every buffer. The library allocates no device memory and keeps
+ *    no pointer after a call returns. Scratch memory comes from the caller's `workspace`, whose
+ *    size the matching *_workspace_size() call returns.
+ *  - Asynchrony: work is enqueued on `hip_stream` (a hipStream_t; NULL = the default stream).
+ *    IKBO_OK means the work was enqueued, not that it finished.
+ *  - Errors: a status code is returned, never an exception. The last failure's text is kept per
+ *    host thread (ikbo_last_error_message). Argument checks run before any GPU work, so a call
+ *    that returns an error other than IKBO_HIP_ERROR has enqueued nothing.
+ *  - Index arrays: cand_to_req (the map m, int32 [num_cand]) and/or req_cand_offsets (int32
+ *    [num_req + 1], candidates of request r are rows off[r]..off[r+1]-1). At least one is
+ *    required. The pages store the candidates of one request contiguously (Sec. 4.2.1); a map
+ *    that is not grouped is accepted too. Index CONTENTS are a precondition that
+ *    ikbo_check_index verifies; kernels stay memory-safe whatever the contents: a candidate
+ *    whose request is out of range gets an all-zero output row.
+ *  - Dtypes: inputs IKBO_F32 or IKBO_BF16; outputs IKBO_F32 or IKBO_BF16; accumulation is
+ *    always fp32. A bf16-output call returns the round-to-nearest-even bf16 of what the same
+ *    call with an fp32 output returns.
+ *  - Results are deterministic run to run (no floating-point atomics).
+ */
+#ifndef IKBO_H
+#define IKBO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IKBO_VERSION 100
+
+/* Status codes */
+#define IKBO_OK 0
+#define IKBO_INVALID_ARGUMENT 1     /* null pointer, negative size, no index array, bad flag */
+#define IKBO_UNSUPPORTED 2          /* dtype combination or head_dim not built */
+#define IKBO_MISALIGNED 3           /* base pointer or row width breaks 16-byte alignment */
+#define IKBO_WORKSPACE_TOO_SMALL 4  /* workspace_bytes below the *_workspace_size() value */
+#define IKBO_HIP_ERROR 5            /* a HIP call or kernel launch failed */
+
+/* Dtype codes */
+#define IKBO_F32 0
+#define IKBO_BF16 1
+
+/* Activations (applied per group, a pointwise GLM op: Sec. 3.1.3, Eq. 8) */
+#define IKBO_ACT_NONE 0
+#define IKBO_ACT_GELU 1             /* exact form x * Phi(x) = x/2 (1 + erf(x / sqrt 2)) */
+
+/* index_flags bits */
+#define IKBO_INDEX_SORTED 1u        /* cand_to_req is non-decreasing (candidates grouped) */
+
+int ikbo_version(void);
+const char *ikbo_status_string(int status);
+const char *ikbo_last_error_message(void);
+
+/* ------------------------------------------------------------------------------------------
+ * IKBO-DCA: candidate-side cross attention of Deep Cross Attention (Sec. 3.2, Eq. 13, the
+ * A^C term), executed as in Sec. 4.3.1: the kernel takes K and V at the request batch size,
+ * resolves each candidate's request, and every candidate of a request reads the same physical
+ * K/V rows.
+ *
+ *   out[c, t, h, :] = sum_j softmax_j(scale * <q[c,t,h,:], k[r,j,h,:]>) * v[r, j, h, :],
+ *   with r the request of candidate c and j over the L_r keys of request r.
+ *
+ * q     [num_cand, q_len, num_heads, head_dim]   (in_dtype)
+ * k, v  uniform: [num_req, kv_len, num_heads, head_dim]; variable length (kv_cu_seqlens set):
+ *       [kv_cu_seqlens[num_req], num_heads, head_dim], request r owning rows
+ *       kv_cu_seqlens[r] .. kv_cu_seqlens[r+1]-1                       (in_dtype)
+ * kv_cu_seqlens  device int32 [num_req + 1] or NULL (uniform length kv_len)
+ * kv_len         uniform K/V length, or with kv_cu_seqlens an upper bound on L_r (0 = unknown)
+ * cand_to_req, req_cand_offsets, index_flags   see the conventions above; when offsets are
+ *       given they define the grouping and cand_to_req is not read.
+ * num_heads      H >= 1 (queries and keys share the head count)
+ * head_dim       bf16: 64 or 128; fp32: a multiple of 4 in [4, 128]
+ * softmax_scale  <= 0 selects 1/sqrt(head_dim)
+ * out   [num_cand, q_len, num_heads, head_dim] (out_dtype). Rows of a request with L_r = 0 and
+ *       rows of candidates with no valid request are written as zeros.
+ * workspace      device scratch of at least ikbo_dca_workspace_size(num_cand, num_req) bytes
+ *       (may be NULL when that size is 0).
+ * Errors: IKBO_INVALID_ARGUMENT, IKBO_UNSUPPORTED, IKBO_MISALIGNED, IKBO_WORKSPACE_TOO_SMALL,
+ *         IKBO_HIP_ERROR.
+ * ---------------------------------------------------------------------------------------- */
+size_t ikbo_dca_workspace_size(int64_t num_cand, int64_t num_req);
+
+int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len,
+                     const void *k, const void *v, int64_t num_req,
+                     const int32_t *kv_cu_seqlens, int32_t kv_len,
+                     const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                     int32_t num_heads, int32_t head_dim, float softmax_scale,
+                     int32_t in_dtype, int32_t out_dtype, void *out,
+                     void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * IKBO-LCB: the GLM-masked two-group linear layer (Sec. 3.1.2, Eq. 4 with the mask of Eq. 3,
+ * block form Eq. 6), run as the decomposition of Sec. 4.1, Eq. 14:
+ *   [y_r ; Z] = [W_RR ; W_CR] x_r          once per request (request batch),
+ *   y_c[c]   = act(W_CC x_c[c] + Z[m(c)] + b_c)   with the Z gather-added in the GEMM epilogue
+ *                                                  (Sec. 4.2.1),
+ *   y_r[r]   = act(W_RR x_r[r] + b_r).
+ * The request<-candidate block W_RC of Eq. 6 is zero by construction and is not an argument.
+ *
+ * x_req  [num_req, k_req], x_cand [num_cand, k_cand]               (in_dtype)
+ * w_rr   [n_req_out, k_req], w_cr [n_cand_out, k_req], w_cc [n_cand_out, k_cand]  (in_dtype)
+ * b_r    [n_req_out] fp32 or NULL;  b_c [n_cand_out] fp32 or NULL
+ * activation  IKBO_ACT_NONE or IKBO_ACT_GELU, applied to both groups
+ * y_req  [num_req, n_req_out] (out_dtype) or NULL to skip the request-group output
+ * y_cand [num_cand, n_cand_out] (out_dtype)
+ * k_req, k_cand, n_req_out, n_cand_out: >= 0; with bf16 the K widths must be multiples of 8 and
+ *       with fp32 multiples of 4 (16-byte rows), else IKBO_MISALIGNED -- the zero padding of
+ *       Sec. 4.2.4 is the caller's transform.
+ * workspace >= ikbo_lcb_workspace_size(num_cand, num_req, k_req, n_req_out, n_cand_out) bytes;
+ *       it holds Z in fp32 and the request GEMM's split-K partial sums.
+ * ---------------------------------------------------------------------------------------- */
+size_t ikbo_lcb_workspace_size(int64_t num_cand, int64_t num_req, int32_t k_req,
+                               int32_t n_req_out, int32_t n_cand_out);
+
+int ikbo_lcb_forward(const void *x_req, int64_t num_req, int32_t k_req,
+                     const void *x_cand, int64_t num_cand, int32_t k_cand,
+                     const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                     const void *w_rr, const void *w_cr, const void *w_cc,
+                     const float *b_r, const float *b_c,
+                     int32_t n_req_out, int32_t n_cand_out, int32_t activation,
+                     int32_t in_dtype, int32_t out_dtype, void *y_req, void *y_cand,
+                     void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * GLM-MLP: a stack of GLM linear layers (each an IKBO-LCB), closed under composition
+ * (Sec. 3.1.5, Eq. 11), as used to form DCA queries (Sec. 3.2, Eq. 12). Layer l+1 takes
+ * layer l's outputs: k_req(l+1) = n_req_out(l), k_cand(l+1) = n_cand_out(l). Hidden
+ * activations live in the workspace, in bf16 for bf16 inputs and fp32 for fp32 inputs; the
+ * last layer writes y_req / y_cand in out_dtype.
+ * `layers` is a HOST array of num_layers descriptors whose pointer members are device
+ * pointers.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct ikbo_glm_layer {
+    const void *w_rr;       /* [n_req_out, k_req] */
+    const void *w_cr;       /* [n_cand_out, k_req] */
+    const void *w_cc;       /* [n_cand_out, k_cand] */
+    const float *b_r;       /* [n_req_out] or NULL */
+    const float *b_c;       /* [n_cand_out] or NULL */
+    int32_t k_req, k_cand, n_req_out, n_cand_out;
+    int32_t activation;
+} ikbo_glm_layer;
+
+size_t ikbo_glm_mlp_workspace_size(int64_t num_cand, int64_t num_req, int32_t num_layers,
+                                   const ikbo_glm_layer *layers, int32_t in_dtype);
+
+int ikbo_glm_mlp_forward(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
+                         const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                         int32_t num_layers, const ikbo_glm_layer *layers,
+                         int32_t in_dtype, int32_t out_dtype, void *y_req, void *y_cand,
+                         void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Index check: counts, on the device, (a) candidates whose cand_to_req is outside
+ * [0, num_req), (b) with IKBO_INDEX_SORTED, candidates whose map value is below the previous
+ * candidate's, (c) when both arrays are given, candidates that are not inside
+ * [off[m(c)], off[m(c)+1]), and (d) offsets that are not a non-decreasing partition of
+ * [0, num_cand) (each bad offset entry counts once, off[0] != 0 and off[R] != C once each).
+ * d_violations: device uint64 [1], overwritten with the count (0 = valid).
+ * ---------------------------------------------------------------------------------------- */
+int ikbo_check_index(const int32_t *cand_to_req, const int32_t *req_cand_offsets,
+                     int64_t num_cand, int64_t num_req, uint32_t index_flags,
+                     uint64_t *d_violations, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IKBO_H */

@@ -1,0 +1,201 @@
+"""fp64 CPU oracle of the IKBO hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package. It shares no code with the GPU library (``request_candidate_broadcast_amd``)
+and never imports it.
+
+The arithmetic lives in ``ikbo_oracle.c`` (plain C, fp64, threaded over candidates). It expands
+every request-side tensor once per candidate -- the materialised broadcast the GPU path avoids --
+then evaluates the definitions:
+
+* ``dca``   candidate cross attention, ROCS Sec. 3.2 Eq. 13 (A^C) with request-batched K/V read
+            through the candidate->request map (Sec. 4.3.1); two-pass softmax.
+* ``glm``   the GLM-masked affine layer stack, Sec. 3.1.2 Eq. 4/6 (explicit zero block), with the
+            per-group activation of Eq. 8, composed as in Sec. 3.1.5 Eq. 11. One layer is the
+            IKBO-LCB linear form; two layers are the query MLP of Eq. 12.
+* ``gelu``  exact GELU x * Phi(x) via libm erf.
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py`` against library
+routines, closed forms, invariants and brute force on tiny inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libikbo_oracle.so")
+SRC_PATH = os.path.join(_HERE, "ikbo_oracle.c")
+
+F32, BF16 = 0, 1
+ACT = {"none": 0, "gelu": 1}
+
+
+def build_lib(force: bool = False) -> str:
+    """Compile the oracle with gcc -O2 (no fast-math, no BLAS)."""
+    if force or not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+        tmp = LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               SRC_PATH, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("w_rr", ctypes.c_void_p), ("w_cr", ctypes.c_void_p), ("w_cc", ctypes.c_void_p),
+                ("b_r", ctypes.c_void_p), ("b_c", ctypes.c_void_p),
+                ("k_req", ctypes.c_int32), ("k_cand", ctypes.c_int32),
+                ("n_req", ctypes.c_int32), ("n_cand", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        build_lib()
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.oracle_gelu.restype = dbl
+        lib.oracle_gelu.argtypes = [dbl]
+        lib.oracle_request_of.restype = i64
+        lib.oracle_request_of.argtypes = [vp, vp, i64, i64]
+        lib.oracle_dca.restype = ctypes.c_int
+        lib.oracle_dca.argtypes = [vp, i64, i32, vp, vp, i64, vp, i32, vp, vp, i32, i32, dbl, i32,
+                                   vp, i64, vp, ctypes.POINTER(ctypes.c_int64), i32]
+        lib.oracle_glm.restype = ctypes.c_int
+        lib.oracle_glm.argtypes = [vp, i64, vp, i64, vp, vp, i32, ctypes.POINTER(_Layer), i32,
+                                   vp, i64, vp, vp, vp, ctypes.POINTER(ctypes.c_int64), i32]
+        lib.oracle_index_violations.restype = i64
+        lib.oracle_index_violations.argtypes = [vp, vp, i64, i64, i32]
+        _lib = lib
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _threads(n: Optional[int]) -> int:
+    return n if n else max(1, min(16, os.cpu_count() or 1))
+
+
+def _dtype_code(arr: np.ndarray) -> int:
+    if arr.dtype == np.uint16:
+        return BF16
+    if arr.dtype == np.float32:
+        return F32
+    raise TypeError("oracle inputs are bf16 bit patterns (uint16) or float32, got %s" % arr.dtype)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def gelu(x: float) -> float:
+    return float(_get().oracle_gelu(float(x)))
+
+
+def request_of(m, off, R: int, c: int) -> int:
+    m, off = _i32(m), _i32(off)
+    return int(_get().oracle_request_of(_ptr(m), _ptr(off), R, c))
+
+
+def dca(q: np.ndarray, k: np.ndarray, v: np.ndarray, R: int, *, m=None, off=None, kv_cu=None,
+        L: Optional[int] = None, scale: Optional[float] = None, cands: Optional[Sequence[int]] = None,
+        nthreads: Optional[int] = None, return_violations: bool = False):
+    """Cross attention of candidate queries over their request's K/V, fp64.
+
+    q [C, Lq, H, d]; k, v [R, L, H, d] or varlen [sum L_r, H, d] with kv_cu [R+1].
+    Returns [n, Lq, H, d] fp64 for the candidates `cands` (all when None)."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    assert _dtype_code(k) == dt and _dtype_code(v) == dt
+    C, Lq, H, d = q.shape
+    m, off, kv_cu = _i32(m), _i32(off), _i32(kv_cu)
+    if kv_cu is None:
+        Lu = k.shape[1] if k.ndim == 4 else (L if L is not None else 0)
+    else:
+        Lu = int(np.max(np.diff(kv_cu))) if R > 0 else 0
+        if L is not None:
+            Lu = max(Lu, L)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    cand_arr = None if cands is None else np.ascontiguousarray(cands, dtype=np.int64)
+    n = C if cand_arr is None else len(cand_arr)
+    out = np.zeros((n, Lq, H, d), dtype=np.float64)
+    viol = ctypes.c_int64(0)
+    rc = _get().oracle_dca(_ptr(q), C, Lq, _ptr(k), _ptr(v), R, _ptr(kv_cu), Lu, _ptr(m), _ptr(off),
+                           H, d, float(scale), dt, _ptr(cand_arr), n, _ptr(out), ctypes.byref(viol),
+                           _threads(nthreads))
+    if rc != 0:
+        raise OracleError("oracle_dca failed with code %d" % rc)
+    return (out, viol.value) if return_violations else out
+
+
+def glm(x_r: np.ndarray, x_c: np.ndarray, layers: Sequence[dict], *, m=None, off=None,
+        cands: Optional[Sequence[int]] = None, want_request_per_cand: bool = False,
+        want_request: bool = False, nthreads: Optional[int] = None, return_violations: bool = False):
+    """GLM-masked layer stack, fp64.
+
+    layers: dicts with w_rr [N_r,K_r], w_cr [N_c,K_r], w_cc [N_c,K_c] (bf16 bits or fp32),
+    b_r, b_c fp32 (or None) and act ("none" | "gelu").
+    Returns dict with y_c [n, N_c], and optionally y_r_c [n, N_r], y_r [R, N_r]."""
+    x_r = np.ascontiguousarray(x_r)
+    x_c = np.ascontiguousarray(x_c)
+    dt = _dtype_code(x_r)
+    assert _dtype_code(x_c) == dt
+    R, C = x_r.shape[0], x_c.shape[0]
+    keep = []
+    arr = (_Layer * len(layers))()
+    for i, ly in enumerate(layers):
+        w_rr = np.ascontiguousarray(ly["w_rr"])
+        w_cr = np.ascontiguousarray(ly["w_cr"])
+        w_cc = np.ascontiguousarray(ly["w_cc"])
+        for w in (w_rr, w_cr, w_cc):
+            assert _dtype_code(w) == dt
+        b_r = None if ly.get("b_r") is None else np.ascontiguousarray(ly["b_r"], dtype=np.float32)
+        b_c = None if ly.get("b_c") is None else np.ascontiguousarray(ly["b_c"], dtype=np.float32)
+        keep += [w_rr, w_cr, w_cc, b_r, b_c]
+        arr[i] = _Layer(w_rr.ctypes.data, w_cr.ctypes.data, w_cc.ctypes.data,
+                        None if b_r is None else b_r.ctypes.data,
+                        None if b_c is None else b_c.ctypes.data,
+                        w_rr.shape[1], w_cc.shape[1], w_rr.shape[0], w_cc.shape[0],
+                        ACT[ly.get("act", "none")])
+    m, off = _i32(m), _i32(off)
+    cand_arr = None if cands is None else np.ascontiguousarray(cands, dtype=np.int64)
+    n = C if cand_arr is None else len(cand_arr)
+    nr, nc = int(arr[len(layers) - 1].n_req), int(arr[len(layers) - 1].n_cand)
+    y_c = np.zeros((n, nc), dtype=np.float64)
+    y_r_c = np.zeros((n, nr), dtype=np.float64) if want_request_per_cand else None
+    y_r = np.zeros((R, nr), dtype=np.float64) if want_request else None
+    viol = ctypes.c_int64(0)
+    rc = _get().oracle_glm(_ptr(x_r), R, _ptr(x_c), C, _ptr(m), _ptr(off), len(layers), arr, dt,
+                           _ptr(cand_arr), n, _ptr(y_c), _ptr(y_r_c), _ptr(y_r), ctypes.byref(viol),
+                           _threads(nthreads))
+    if rc != 0:
+        raise OracleError("oracle_glm failed with code %d" % rc)
+    out = {"y_c": y_c}
+    if want_request_per_cand:
+        out["y_r_c"] = y_r_c
+    if want_request:
+        out["y_r"] = y_r
+    if return_violations:
+        out["violations"] = viol.value
+    return out
+
+
+def index_violations(m, off, C: int, R: int, sorted_flag: bool = False) -> int:
+    m, off = _i32(m), _i32(off)
+    return int(_get().oracle_index_violations(_ptr(m), _ptr(off), C, R, 1 if sorted_flag else 0))
