@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the IKBO hot path on one MI355X.
+
+Default workload ("block"): the full ROCS block at production-like scale, bf16 --
+R = 128 requests x 2048 candidates; a 2-layer GLM-masked MLP over [request 4096 | candidate 2048]
+features (hidden 2048 per group, GELU; output 4096 per group = 4 query tokens x 8 heads x 128)
+feeds IKBO-DCA over a shared request history of L = 8192 keys (H = 8, d = 128). One step = one
+ikbo_glm_mlp_forward (two IKBO-LCB layers) + one ikbo_dca_forward on the same stream, inputs
+resident in HBM. Other workloads (--workload dca_fixed | dca_ragged | lcb) time a single operator.
+
+Prints ONE JSON line: throughput in effective TFLOP/s (no broadcast counted), ms per step, the
+roofline of the dominant kernel from HIP events on its stream, and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "IKBO-DCA TFLOP/s + ms; IKBO-LCB ms; % of MI355X bf16 MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="block", choices=["block", "dca_fixed", "dca_ragged", "lcb"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=0, help="candidates in the oracle sample (0 = default)")
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                   help="per-kernel HBM bytes measured with rocprofv3 counters, if present")
+    return p.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import request_candidate_broadcast_amd as ikbo
+    import synth
+
+    if not os.path.exists(ikbo.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    ikbo.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()   # default priority
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        if a.dtype == np.int32 or a.dtype == np.int64:
+            return torch.from_numpy(a.astype(np.int32)).to(dev)
+        return torch.from_numpy(a.astype(np.float32)).to(dev)
+
+    t_gen = time.time()
+    parts = {}          # name -> (list of event pairs)
+    flops = {}
+    algo_bytes = {}
+    with torch.cuda.stream(stream):
+        if args.workload in ("block",):
+            g, s = synth.block_specs()
+            x_r = up(synth.glm_x(g, "x_r"))
+            x_c = up(synth.glm_x(g, "x_c"))
+            layers = []
+            for li in range(len(g.layers)):
+                w = synth.glm_weights(g, li)
+                layers.append({"w_rr": up(w["w_rr"]), "w_cr": up(w["w_cr"]), "w_cc": up(w["w_cc"]),
+                               "b_r": up(w["b_r"]), "b_c": up(w["b_c"]), "act": g.layers[li].act})
+            k = up(synth.dca_kv(s, "k")).view(s.R, s.L, s.H, s.d)
+            v = up(synth.dca_kv(s, "v")).view(s.R, s.L, s.H, s.d)
+            off = up(s.offsets)
+            m = up(s.cand_to_req)
+            last = g.layers[-1]
+            y_req = torch.empty((g.R, last.n_req), dtype=torch.bfloat16, device=dev)
+            y_cand = torch.empty((g.C, last.n_cand), dtype=torch.bfloat16, device=dev)
+            q = y_cand.view(s.C, s.Lq, s.H, s.d)
+            out = torch.empty((s.C, s.Lq, s.H, s.d), dtype=torch.bfloat16, device=dev)
+            ws_mlp = torch.empty(ikbo.ikbo_glm_mlp_workspace_size(g.C, g.R, layers, torch.bfloat16),
+                                 dtype=torch.uint8, device=dev)
+            ws_dca = torch.empty(max(1, ikbo.ikbo_dca_workspace_size(s.C, s.R)), dtype=torch.uint8, device=dev)
+            flops["mlp"] = g.flops()
+            flops["dca"] = s.flops()
+            algo_bytes["dca"] = 2 * (s.C * s.Lq * s.H * s.d) * 2 + 2 * (s.R * s.L * s.H * s.d) * 2 + 4 * s.C
+            ly0, ly1 = g.layers
+            algo_bytes["mlp"] = 2 * (g.C * (ly0.k_cand + ly0.n_cand + ly1.n_cand + ly1.n_cand)
+                                     + g.R * (ly0.k_req + ly0.n_req + ly1.n_req))
+
+            def step(ev):
+                ev[0].record(stream)
+                ikbo.ikbo_glm_mlp_forward(x_r, x_c, layers, cand_to_req=m, sorted_index=True, y_req=y_req,
+                                          y_cand=y_cand, workspace=ws_mlp, stream=stream)
+                ev[1].record(stream)
+                ikbo.ikbo_dca_forward(q, k, v, req_cand_offsets=off, out=out, workspace=ws_dca, stream=stream)
+                ev[2].record(stream)
+
+            names = [("mlp", 0, 1), ("dca", 1, 2)]
+            dominant = "dca"
+            config = {"workload": "full ROCS block: GLM-MLP (2 IKBO-LCB layers) -> IKBO-DCA",
+                      "requests": s.R, "candidates": s.C, "cand_per_request": int(s.counts[0]),
+                      "mlp": "[4096|2048] -> 2048 (GELU) -> 4096", "kv_len": s.L, "heads": s.H, "head_dim": s.d,
+                      "q_tokens": s.Lq}
+        elif args.workload in ("dca_fixed", "dca_ragged"):
+            s = synth.dca_spec(args.workload)
+            q = up(synth.dca_q(s))
+            k, v = up(synth.dca_kv(s, "k")), up(synth.dca_kv(s, "v"))
+            kw = {}
+            if s.varlen:
+                kw["kv_cu_seqlens"] = up(s.kv_cu)
+            else:
+                k = k.view(s.R, s.L, s.H, s.d)
+                v = v.view(s.R, s.L, s.H, s.d)
+            off = up(s.offsets)
+            out = torch.empty((s.C, s.Lq, s.H, s.d), dtype=torch.bfloat16, device=dev)
+            ws_dca = torch.empty(max(1, ikbo.ikbo_dca_workspace_size(s.C, s.R)), dtype=torch.uint8, device=dev)
+            flops["dca"] = s.flops()
+            algo_bytes["dca"] = 2 * (s.C * s.Lq * s.H * s.d) * 2 + 2 * (s.kv_rows * s.H * s.d) * 2 + 4 * s.C
+
+            def step(ev):
+                ev[0].record(stream)
+                ikbo.ikbo_dca_forward(q, k, v, num_req=s.R, req_cand_offsets=off, out=out, workspace=ws_dca,
+                                      stream=stream, **kw)
+                ev[1].record(stream)
+
+            names = [("dca", 0, 1)]
+            dominant = "dca"
+            config = {"workload": "IKBO-DCA " + args.workload, "requests": s.R, "candidates": s.C,
+                      "kv_len": "varlen" if s.varlen else s.L, "heads": s.H, "head_dim": s.d, "q_tokens": s.Lq}
+        else:
+            g = synth.glm_spec("lcb")
+            x_r = up(synth.glm_x(g, "x_r"))
+            x_c = up(synth.glm_x(g, "x_c"))
+            w = synth.glm_weights(g, 0)
+            wd = {kk: up(vv) for kk, vv in w.items()}
+            m = up(g.cand_to_req)
+            ly = g.layers[0]
+            y_req = torch.empty((g.R, ly.n_req), dtype=torch.bfloat16, device=dev)
+            y_cand = torch.empty((g.C, ly.n_cand), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(ikbo.ikbo_lcb_workspace_size(g.C, g.R, ly.k_req, ly.n_req, ly.n_cand), dtype=torch.uint8,
+                             device=dev)
+            flops["lcb"] = g.flops()
+            algo_bytes["lcb"] = 2 * (g.C * (ly.k_cand + ly.n_cand) + g.R * (ly.k_req + ly.n_req)
+                                     + (ly.n_req + ly.n_cand) * ly.k_req + ly.n_cand * ly.k_cand) + 4 * g.C
+
+            def step(ev):
+                ev[0].record(stream)
+                ikbo.ikbo_lcb_forward(x_r, x_c, wd["w_rr"], wd["w_cr"], wd["w_cc"], b_r=wd["b_r"], b_c=wd["b_c"],
+                                      cand_to_req=m, sorted_index=True, activation="gelu", y_req=y_req, y_cand=y_cand,
+                                      workspace=ws, stream=stream)
+                ev[1].record(stream)
+
+            names = [("lcb", 0, 1)]
+            dominant = "lcb"
+            config = {"workload": "IKBO-LCB broadcast-fused GLM linear", "requests": g.R, "candidates": g.C,
+                      "k_req": ly.k_req, "k_cand": ly.k_cand, "n_out": ly.n_cand, "activation": "gelu"}
+    torch.cuda.synchronize()
+    log("inputs ready in %.1f s (%s)" % (time.time() - t_gen, args.workload))
+
+    nev = max(e for _, _, e in names) + 1
+    warm = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(max(args.warmup, 0))]
+    timed = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        step(warm[i])
+        torch.cuda.synchronize()
+        log("warmup step %d done" % i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(timed[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    log("timed %d steps: %.3f ms/step" % (args.steps, ms_step))
+
+    per = {}
+    for name, a, b in names:
+        d = [timed[i][a].elapsed_time(timed[i][b]) for i in range(args.steps)]
+        per[name] = {"ms_avg": float(np.mean(d)), "ms_min": float(np.min(d)), "ms_median": float(np.median(d))}
+        per[name]["tflops"] = flops[name] / (per[name]["ms_avg"] * 1e-3) / 1e12
+        per[name]["gbs_algorithmic"] = algo_bytes[name] / (per[name]["ms_avg"] * 1e-3) / 1e9
+        per[name]["mfma_frac"] = per[name]["tflops"] / PEAK_BF16_TFLOPS
+    total_flops = sum(flops.values())
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    # roofline of the dominant kernel (its own events on its stream)
+    dk = per[dominant]
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        ent = tj.get(args.workload, {}).get(dominant)
+        if ent:
+            traffic = ent.get("bytes_per_launch")
+    except (OSError, ValueError):
+        traffic = None
+    roofline = {"bound": "mfma", "achieved": round(dk["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dk["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": dominant, "flops_per_launch": flops[dominant], "ms_per_launch": round(dk["ms_avg"], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, np)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded SplitMix64 normals)",
+        "config": config,
+        "parts": {k: {kk: round(vv, 4) for kk, vv in d.items()} for k, d in per.items()},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(args, np):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload (all host threads it uses)."""
+    import oracle
+    import synth
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    if args.workload == "block":
+        g, s = synth.block_specs()
+        n_per = args.cpu_sample // 4 if args.cpu_sample else 8
+        reqs = [0, 1, g.R // 2, g.R - 1]
+        off = g.offsets
+        # compact inputs: the sampled candidates' rows, and the K/V blocks of their requests only
+        x_r = synth.glm_x(g, "x_r")
+        x_c = np.concatenate([synth.glm_x(g, "x_c", int(off[r]), n_per) for r in reqs])
+        m_sub = np.repeat(np.array(reqs, np.int32), n_per)
+        layers = [dict(synth.glm_weights(g, li), act=g.layers[li].act) for li in range(len(g.layers))]
+        k = np.stack([synth.dca_kv_request(s, "k", r) for r in reqs])
+        v = np.stack([synth.dca_kv_request(s, "v", r) for r in reqs])
+        m_kv = np.repeat(np.arange(len(reqs), dtype=np.int32), n_per)
+        n = len(m_sub)
+        log("cpu baseline: oracle on %d candidates with %d threads" % (n, nthreads))
+        t0 = time.perf_counter()
+        qo = oracle.glm(x_r, x_c, layers, m=m_sub, nthreads=nthreads)["y_c"]
+        oracle.dca(qo.reshape(n, s.Lq, s.H, s.d), k, v, len(reqs), m=m_kv, nthreads=nthreads)
+        secs = time.perf_counter() - t0
+        work = (g.flops() + s.flops()) / g.C * n
+        sample = "%d candidates (the first %d of requests %s): GLM-MLP then DCA, chained in fp64" % (n, n_per, reqs)
+    elif args.workload in ("dca_fixed", "dca_ragged"):
+        s = synth.dca_spec(args.workload)
+        reqs = [0, 1, s.R // 2, s.R - 1]
+        n_per = args.cpu_sample // 4 if args.cpu_sample else 16
+        off = s.offsets
+        cands = np.concatenate([np.arange(off[r], min(off[r] + n_per, off[r + 1])) for r in reqs]).astype(np.int64)
+        q = synth.dca_q(s)
+        k, v = synth.dca_kv(s, "k"), synth.dca_kv(s, "v")
+        kw = {"kv_cu": s.kv_cu} if s.varlen else {}
+        if not s.varlen:
+            k = k.reshape(s.R, s.L, s.H, s.d)
+            v = v.reshape(s.R, s.L, s.H, s.d)
+        t0 = time.perf_counter()
+        oracle.dca(q, k, v, s.R, m=s.cand_to_req, cands=cands, nthreads=nthreads, **kw)
+        secs = time.perf_counter() - t0
+        work = 4.0 * s.Lq * s.H * s.d * float(np.sum(s.kv_lens[s.cand_to_req[cands]]))
+        sample = "%d candidates of requests %s" % (len(cands), reqs)
+    else:
+        g = synth.glm_spec("lcb")
+        reqs = [0, 1, g.R // 2, g.R - 1]
+        n_per = args.cpu_sample // 4 if args.cpu_sample else 64
+        off = g.offsets
+        cands = np.concatenate([np.arange(off[r], off[r] + n_per) for r in reqs]).astype(np.int64)
+        x_r, x_c = synth.glm_x(g, "x_r"), synth.glm_x(g, "x_c")
+        ly = dict(synth.glm_weights(g, 0), act="gelu")
+        t0 = time.perf_counter()
+        oracle.glm(x_r, x_c, [ly], m=g.cand_to_req, cands=cands, nthreads=nthreads)
+        secs = time.perf_counter() - t0
+        work = g.flops() / g.C * len(cands)
+        sample = "%d candidates of requests %s" % (len(cands), reqs)
+    log("cpu baseline: %.1f s" % secs)
+    return {"value": round(work / secs / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": sample, "seconds": round(secs, 2)}
+
+
+if __name__ == "__main__":
+    main()

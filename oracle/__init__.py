@@ -31,7 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libikbo_oracle.so")
 SRC_PATH = os.path.join(_HERE, "ikbo_oracle.c")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 ACT = {"none": 0, "gelu": 1}
 
 
@@ -66,7 +66,7 @@ def _get():
         lib.oracle_request_of.restype = i64
         lib.oracle_request_of.argtypes = [vp, vp, i64, i64]
         lib.oracle_dca.restype = ctypes.c_int
-        lib.oracle_dca.argtypes = [vp, i64, i32, vp, vp, i64, vp, i32, vp, vp, i32, i32, dbl, i32,
+        lib.oracle_dca.argtypes = [vp, i64, i32, vp, vp, i64, vp, i32, vp, vp, i32, i32, dbl, i32, i32,
                                    vp, i64, vp, ctypes.POINTER(ctypes.c_int64), i32]
         lib.oracle_glm.restype = ctypes.c_int
         lib.oracle_glm.argtypes = [vp, i64, vp, i64, vp, vp, i32, ctypes.POINTER(_Layer), i32,
@@ -116,12 +116,14 @@ def dca(q: np.ndarray, k: np.ndarray, v: np.ndarray, R: int, *, m=None, off=None
     """Cross attention of candidate queries over their request's K/V, fp64.
 
     q [C, Lq, H, d]; k, v [R, L, H, d] or varlen [sum L_r, H, d] with kv_cu [R+1].
-    Returns [n, Lq, H, d] fp64 for the candidates `cands` (all when None)."""
+    q may also be float64 (a chained fp64 query). Returns [n, Lq, H, d] fp64 for the candidates
+    `cands` (all when None)."""
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
     v = np.ascontiguousarray(v)
-    dt = _dtype_code(q)
-    assert _dtype_code(k) == dt and _dtype_code(v) == dt
+    dt = _dtype_code(k)
+    assert _dtype_code(v) == dt
+    qdt = F64 if q.dtype == np.float64 else _dtype_code(q)
     C, Lq, H, d = q.shape
     m, off, kv_cu = _i32(m), _i32(off), _i32(kv_cu)
     if kv_cu is None:
@@ -137,7 +139,7 @@ def dca(q: np.ndarray, k: np.ndarray, v: np.ndarray, R: int, *, m=None, off=None
     out = np.zeros((n, Lq, H, d), dtype=np.float64)
     viol = ctypes.c_int64(0)
     rc = _get().oracle_dca(_ptr(q), C, Lq, _ptr(k), _ptr(v), R, _ptr(kv_cu), Lu, _ptr(m), _ptr(off),
-                           H, d, float(scale), dt, _ptr(cand_arr), n, _ptr(out), ctypes.byref(viol),
+                           H, d, float(scale), dt, qdt, _ptr(cand_arr), n, _ptr(out), ctypes.byref(viol),
                            _threads(nthreads))
     if rc != 0:
         raise OracleError("oracle_dca failed with code %d" % rc)

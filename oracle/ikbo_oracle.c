@@ -32,12 +32,13 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
 enum { OR_ACT_NONE = 0, OR_ACT_GELU = 1 };
 enum { OR_OK = 0, OR_BAD_ARG = -1, OR_INDEX_DISAGREE = -2, OR_NO_MEMORY = -3 };
 
 /* Widen one stored element to double (bf16 is the top half of an IEEE fp32). */
 static double in_at(const void *p, int dtype, int64_t i) {
+    if (dtype == OR_F64) return ((const double *)p)[i];
     if (dtype == OR_F32) return (double)((const float *)p)[i];
     uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
     float f;
@@ -123,7 +124,7 @@ static int parallel_for(int64_t n, int nthreads, size_t scratch_bytes, item_fn f
 
 typedef struct {
     const void *q, *k, *v;
-    int dtype;
+    int dtype, qdtype;
     int64_t C, R;
     int Lq, H, d, L;
     const int32_t *kv_cu, *m, *off;
@@ -168,7 +169,7 @@ static void dca_item(void *vctx, int64_t i, void *scratch) {
             /* scores s_j = scale * <q, k_j> */
             for (int64_t j = 0; j < Lr; ++j) {
                 double acc = 0.0;
-                for (int e = 0; e < d; ++e) acc += in_at(x->q, x->dtype, qrow + e) * Kc[(j * H + h) * d + e];
+                for (int e = 0; e < d; ++e) acc += in_at(x->q, x->qdtype, qrow + e) * Kc[(j * H + h) * d + e];
                 s[j] = x->scale * acc;
             }
             /* softmax over the keys, two passes: max, then exp and sum */
@@ -189,19 +190,21 @@ static void dca_item(void *vctx, int64_t i, void *scratch) {
 /* out: [n, Lq, H, d] fp64 for the candidates cands[0..n) (or all C when cands is NULL).
  * kv_cu: [R+1] prefix offsets of variable K/V lengths, or NULL for uniform length L.
  * L: the uniform length, or the largest L_r when kv_cu is given (sizes the expansion buffer).
+ * dtype: storage of k and v; qdtype: storage of q (fp64 lets a chained oracle stay in fp64).
  * Returns OR_OK, or a negative code; *violations counts rows with an invalid request. */
 int oracle_dca(const void *q, int64_t C, int Lq, const void *k, const void *v, int64_t R,
                const int32_t *kv_cu, int L, const int32_t *m, const int32_t *off, int H, int d,
-               double scale, int dtype, const int64_t *cands, int64_t n, double *out,
+               double scale, int dtype, int qdtype, const int64_t *cands, int64_t n, double *out,
                int64_t *violations, int nthreads) {
     if (!q || !k || !v || !out || (!m && !off) || C < 0 || R < 0 || Lq <= 0 || H <= 0 || d <= 0 || L < 0)
         return OR_BAD_ARG;
     if (dtype != OR_F32 && dtype != OR_BF16) return OR_BAD_ARG;
+    if (qdtype != OR_F32 && qdtype != OR_BF16 && qdtype != OR_F64) return OR_BAD_ARG;
     if (!cands) n = C;
     if (kv_cu)
         for (int64_t r = 0; r < R; ++r)
             if (kv_cu[r + 1] - kv_cu[r] > L) return OR_BAD_ARG;
-    dca_ctx x = {q, k, v, dtype, C, R, Lq, H, d, L, kv_cu, m, off, scale, cands, out, 0, 0};
+    dca_ctx x = {q, k, v, dtype, qdtype, C, R, Lq, H, d, L, kv_cu, m, off, scale, cands, out, 0, 0};
     x.viol = (int64_t *)calloc((size_t)(n > 0 ? n : 1), sizeof(int64_t));
     x.disagree = (int *)calloc((size_t)(n > 0 ? n : 1), sizeof(int));
     if (!x.viol || !x.disagree) { free(x.viol); free(x.disagree); return OR_NO_MEMORY; }

@@ -1,0 +1,309 @@
+"""MI355X-native IKBO hot path: In-Kernel Broadcast Optimization from ROCS (arXiv 2607.27744).
+
+Python binding of ``libikbo.so`` (HIP kernels for gfx950 behind a C ABI, see ``include/ikbo.h``).
+This module only marshals arguments: it turns torch tensors into device pointers, the current
+HIP stream and workspace buffers, and calls the C entry points of the same names. Every step of
+the computation runs in the library's kernels; there is no fallback. If the library is missing
+the calls raise.
+
+Entry points (tensor level):
+
+* ``ikbo_dca_forward``      candidate cross attention over shared request K/V (ROCS Eq. 13, A^C)
+* ``ikbo_lcb_forward``      GLM-masked linear layer with the request term gather-added (Eq. 6, 14)
+* ``ikbo_glm_mlp_forward``  a stack of such layers (Eq. 11-12)
+* ``ikbo_check_index``      device-side validation of the candidate -> request index
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libikbo.so")
+
+IKBO_OK, IKBO_INVALID_ARGUMENT, IKBO_UNSUPPORTED, IKBO_MISALIGNED, IKBO_WORKSPACE_TOO_SMALL, IKBO_HIP_ERROR = range(6)
+IKBO_F32, IKBO_BF16 = 0, 1
+IKBO_ACT_NONE, IKBO_ACT_GELU = 0, 1
+IKBO_INDEX_SORTED = 1
+
+ACTIVATIONS = {"none": IKBO_ACT_NONE, "gelu": IKBO_ACT_GELU, None: IKBO_ACT_NONE}
+
+
+class IkboError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_STATUS_NAMES.get(status, str(status)), message))
+        self.status = status
+
+
+_STATUS_NAMES = {0: "IKBO_OK", 1: "IKBO_INVALID_ARGUMENT", 2: "IKBO_UNSUPPORTED", 3: "IKBO_MISALIGNED",
+                 4: "IKBO_WORKSPACE_TOO_SMALL", 5: "IKBO_HIP_ERROR"}
+
+
+class GlmLayer(ctypes.Structure):
+    """Mirror of ``ikbo_glm_layer``."""
+    _fields_ = [("w_rr", ctypes.c_void_p), ("w_cr", ctypes.c_void_p), ("w_cc", ctypes.c_void_p),
+                ("b_r", ctypes.c_void_p), ("b_c", ctypes.c_void_p),
+                ("k_req", ctypes.c_int32), ("k_cand", ctypes.c_int32),
+                ("n_req_out", ctypes.c_int32), ("n_cand_out", ctypes.c_int32),
+                ("activation", ctypes.c_int32)]
+
+
+EXPORTS = ["ikbo_version", "ikbo_status_string", "ikbo_last_error_message",
+           "ikbo_dca_workspace_size", "ikbo_dca_forward",
+           "ikbo_lcb_workspace_size", "ikbo_lcb_forward",
+           "ikbo_glm_mlp_workspace_size", "ikbo_glm_mlp_forward", "ikbo_check_index"]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libikbo.so and declare its C signatures. Raises when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libikbo.so is not built at %s; run `python -c 'import __graft_entry__ as g; g.build()'`"
+                           % path)
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
+                                  ctypes.c_float, ctypes.c_size_t)
+    lib.ikbo_version.restype = ctypes.c_int
+    lib.ikbo_version.argtypes = []
+    lib.ikbo_status_string.restype = ctypes.c_char_p
+    lib.ikbo_status_string.argtypes = [ctypes.c_int]
+    lib.ikbo_last_error_message.restype = ctypes.c_char_p
+    lib.ikbo_last_error_message.argtypes = []
+    lib.ikbo_dca_workspace_size.restype = sz
+    lib.ikbo_dca_workspace_size.argtypes = [i64, i64]
+    lib.ikbo_dca_forward.restype = ctypes.c_int
+    lib.ikbo_dca_forward.argtypes = [vp, i64, i32, vp, vp, i64, vp, i32, vp, vp, u32, i32, i32, f32, i32, i32, vp,
+                                     vp, sz, vp]
+    lib.ikbo_lcb_workspace_size.restype = sz
+    lib.ikbo_lcb_workspace_size.argtypes = [i64, i64, i32, i32, i32]
+    lib.ikbo_lcb_forward.restype = ctypes.c_int
+    lib.ikbo_lcb_forward.argtypes = [vp, i64, i32, vp, i64, i32, vp, vp, u32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                     i32, vp, vp, vp, sz, vp]
+    lib.ikbo_glm_mlp_workspace_size.restype = sz
+    lib.ikbo_glm_mlp_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(GlmLayer), i32]
+    lib.ikbo_glm_mlp_forward.restype = ctypes.c_int
+    lib.ikbo_glm_mlp_forward.argtypes = [vp, i64, vp, i64, vp, vp, u32, i32, ctypes.POINTER(GlmLayer), i32, i32, vp,
+                                         vp, vp, sz, vp]
+    lib.ikbo_check_index.restype = ctypes.c_int
+    lib.ikbo_check_index.argtypes = [vp, vp, i64, i64, u32, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != IKBO_OK:
+        msg = load_library().ikbo_last_error_message().decode(errors="replace")
+        raise IkboError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return IKBO_BF16
+    if t.dtype == torch.float32:
+        return IKBO_F32
+    raise TypeError("IKBO kernels take bfloat16 or float32 tensors, got %s" % t.dtype)
+
+
+def _torch_dtype(code: int):
+    return torch.bfloat16 if code == IKBO_BF16 else torch.float32
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need_contig(name: str, t: Optional[torch.Tensor]):
+    if t is not None and not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _index(t, name):
+    if t is None:
+        return None
+    if t.dtype != torch.int32:
+        raise TypeError("%s must be int32" % name)
+    _need_contig(name, t)
+    return t
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if workspace is not None:
+        return workspace
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def version() -> int:
+    return int(load_library().ikbo_version())
+
+
+# ------------------------------------------------------------------------------------------------
+def ikbo_dca_workspace_size(num_cand: int, num_req: int) -> int:
+    return int(load_library().ikbo_dca_workspace_size(num_cand, num_req))
+
+
+def ikbo_dca_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, num_req: Optional[int] = None,
+                     cand_to_req: Optional[torch.Tensor] = None, req_cand_offsets: Optional[torch.Tensor] = None,
+                     kv_cu_seqlens: Optional[torch.Tensor] = None, kv_len: Optional[int] = None,
+                     sorted_index: bool = False, softmax_scale: float = 0.0, out_dtype=None,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """IKBO-DCA. q [C, Lq, H, d]; k, v [R, L, H, d] or varlen [sum L_r, H, d] with kv_cu_seqlens [R+1].
+
+    Returns out [C, Lq, H, d] in out_dtype (default: q's dtype)."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_contig(n, t)
+    C, Lq, H, d = q.shape
+    cand_to_req = _index(cand_to_req, "cand_to_req")
+    req_cand_offsets = _index(req_cand_offsets, "req_cand_offsets")
+    kv_cu_seqlens = _index(kv_cu_seqlens, "kv_cu_seqlens")
+    if num_req is None:
+        if kv_cu_seqlens is not None:
+            num_req = kv_cu_seqlens.numel() - 1
+        elif req_cand_offsets is not None:
+            num_req = req_cand_offsets.numel() - 1
+        elif k.dim() == 4:
+            num_req = k.shape[0]
+        else:
+            raise ValueError("num_req is needed")
+    if kv_len is None:
+        kv_len = k.shape[1] if (kv_cu_seqlens is None and k.dim() == 4) else 0
+    in_code = _dt(q)
+    out_code = in_code if out_dtype is None else _dt(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty((C, Lq, H, d), dtype=_torch_dtype(out_code), device=q.device)
+    else:
+        out_code = _dt(out)
+    ws = _workspace(ikbo_dca_workspace_size(C, num_req), q.device, workspace)
+    st = lib.ikbo_dca_forward(_ptr(q), C, Lq, _ptr(k), _ptr(v), num_req, _ptr(kv_cu_seqlens), kv_len,
+                              _ptr(cand_to_req), _ptr(req_cand_offsets), IKBO_INDEX_SORTED if sorted_index else 0,
+                              H, d, float(softmax_scale), in_code, out_code, _ptr(out), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(stream))
+    _check(st)
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+def ikbo_lcb_workspace_size(num_cand: int, num_req: int, k_req: int, n_req_out: int, n_cand_out: int) -> int:
+    return int(load_library().ikbo_lcb_workspace_size(num_cand, num_req, k_req, n_req_out, n_cand_out))
+
+
+def ikbo_lcb_forward(x_req: torch.Tensor, x_cand: torch.Tensor, w_rr: torch.Tensor, w_cr: torch.Tensor,
+                     w_cc: torch.Tensor, *, b_r: Optional[torch.Tensor] = None, b_c: Optional[torch.Tensor] = None,
+                     cand_to_req: Optional[torch.Tensor] = None, req_cand_offsets: Optional[torch.Tensor] = None,
+                     sorted_index: bool = False, activation: str = "none", out_dtype=None,
+                     want_request_output: bool = True, y_req: Optional[torch.Tensor] = None,
+                     y_cand: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """IKBO-LCB. x_req [R, K_r], x_cand [C, K_c], w_rr [N_r, K_r], w_cr [N_c, K_r], w_cc [N_c, K_c].
+
+    Returns (y_req [R, N_r] or None, y_cand [C, N_c])."""
+    lib = load_library()
+    for n, t in (("x_req", x_req), ("x_cand", x_cand), ("w_rr", w_rr), ("w_cr", w_cr), ("w_cc", w_cc),
+                 ("b_r", b_r), ("b_c", b_c)):
+        _need_contig(n, t)
+    for n, t in (("b_r", b_r), ("b_c", b_c)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("%s must be float32" % n)
+    R, K_r = x_req.shape
+    C, K_c = x_cand.shape
+    N_r, N_c = w_rr.shape[0], w_cc.shape[0]
+    cand_to_req = _index(cand_to_req, "cand_to_req")
+    req_cand_offsets = _index(req_cand_offsets, "req_cand_offsets")
+    in_code = _dt(x_req)
+    out_code = in_code if out_dtype is None else _dt(torch.empty(0, dtype=out_dtype))
+    dev = x_cand.device
+    if y_cand is None:
+        y_cand = torch.empty((C, N_c), dtype=_torch_dtype(out_code), device=dev)
+    if want_request_output and y_req is None:
+        y_req = torch.empty((R, N_r), dtype=_torch_dtype(out_code), device=dev)
+    ws = _workspace(ikbo_lcb_workspace_size(C, R, K_r, N_r, N_c), dev, workspace)
+    st = lib.ikbo_lcb_forward(_ptr(x_req), R, K_r, _ptr(x_cand), C, K_c, _ptr(cand_to_req), _ptr(req_cand_offsets),
+                              IKBO_INDEX_SORTED if sorted_index else 0, _ptr(w_rr), _ptr(w_cr), _ptr(w_cc),
+                              _ptr(b_r), _ptr(b_c), N_r, N_c, ACTIVATIONS[activation], in_code, out_code,
+                              _ptr(y_req), _ptr(y_cand), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(st)
+    return y_req, y_cand
+
+
+# ------------------------------------------------------------------------------------------------
+def _layer_structs(layers: Sequence[dict]):
+    arr = (GlmLayer * len(layers))()
+    for i, ly in enumerate(layers):
+        for n in ("w_rr", "w_cr", "w_cc", "b_r", "b_c"):
+            _need_contig(n, ly.get(n))
+        arr[i] = GlmLayer(_ptr(ly["w_rr"]), _ptr(ly["w_cr"]), _ptr(ly["w_cc"]), _ptr(ly.get("b_r")),
+                          _ptr(ly.get("b_c")), ly["w_rr"].shape[1], ly["w_cc"].shape[1], ly["w_rr"].shape[0],
+                          ly["w_cc"].shape[0], ACTIVATIONS[ly.get("act", "none")])
+    return arr
+
+
+def ikbo_glm_mlp_workspace_size(num_cand: int, num_req: int, layers: Sequence[dict], in_dtype) -> int:
+    arr = _layer_structs(layers)
+    return int(load_library().ikbo_glm_mlp_workspace_size(num_cand, num_req, len(layers), arr,
+                                                          _dt(torch.empty(0, dtype=in_dtype))))
+
+
+def ikbo_glm_mlp_forward(x_req: torch.Tensor, x_cand: torch.Tensor, layers: Sequence[dict], *,
+                         cand_to_req: Optional[torch.Tensor] = None, req_cand_offsets: Optional[torch.Tensor] = None,
+                         sorted_index: bool = False, out_dtype=None, want_request_output: bool = True,
+                         y_req: Optional[torch.Tensor] = None, y_cand: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """GLM-MLP. layers: dicts with w_rr, w_cr, w_cc (input dtype), b_r, b_c (fp32 or None), act.
+
+    Returns (y_req [R, N_r(last)] or None, y_cand [C, N_c(last)])."""
+    lib = load_library()
+    _need_contig("x_req", x_req)
+    _need_contig("x_cand", x_cand)
+    R, C = x_req.shape[0], x_cand.shape[0]
+    cand_to_req = _index(cand_to_req, "cand_to_req")
+    req_cand_offsets = _index(req_cand_offsets, "req_cand_offsets")
+    in_code = _dt(x_req)
+    out_code = in_code if out_dtype is None else _dt(torch.empty(0, dtype=out_dtype))
+    arr = _layer_structs(layers)
+    last = layers[-1]
+    dev = x_cand.device
+    if y_cand is None:
+        y_cand = torch.empty((C, last["w_cc"].shape[0]), dtype=_torch_dtype(out_code), device=dev)
+    if want_request_output and y_req is None:
+        y_req = torch.empty((R, last["w_rr"].shape[0]), dtype=_torch_dtype(out_code), device=dev)
+    nbytes = int(lib.ikbo_glm_mlp_workspace_size(C, R, len(layers), arr, in_code))
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib.ikbo_glm_mlp_forward(_ptr(x_req), R, _ptr(x_cand), C, _ptr(cand_to_req), _ptr(req_cand_offsets),
+                                  IKBO_INDEX_SORTED if sorted_index else 0, len(layers), arr, in_code, out_code,
+                                  _ptr(y_req), _ptr(y_cand), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream))
+    _check(st)
+    return y_req, y_cand
+
+
+# ------------------------------------------------------------------------------------------------
+def ikbo_check_index(num_cand: int, num_req: int, *, cand_to_req: Optional[torch.Tensor] = None,
+                     req_cand_offsets: Optional[torch.Tensor] = None, sorted_index: bool = False,
+                     stream=None) -> int:
+    """Number of index violations (0 = valid). Synchronises the stream to read the count."""
+    lib = load_library()
+    cand_to_req = _index(cand_to_req, "cand_to_req")
+    req_cand_offsets = _index(req_cand_offsets, "req_cand_offsets")
+    dev = (cand_to_req if cand_to_req is not None else req_cand_offsets).device
+    cnt = torch.empty(1, dtype=torch.int64, device=dev)
+    st = lib.ikbo_check_index(_ptr(cand_to_req), _ptr(req_cand_offsets), num_cand, num_req,
+                              IKBO_INDEX_SORTED if sorted_index else 0, _ptr(cnt), _stream(stream))
+    _check(st)
+    return int(cnt.item())

@@ -1,0 +1,452 @@
+// The C ABI of libikbo (declared in include/ikbo.h): argument checks, workspace carving and
+// kernel launches on the caller's stream. No device memory is allocated here.
+#include "ikbo.h"
+#include "ikbo_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return IKBO_OK;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+    return fail(IKBO_HIP_ERROR, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define IKBO_HIP(call)                                   \
+    do {                                                 \
+        hipError_t e_ = (call);                          \
+        if (e_ != hipSuccess) return hip_fail(e_, #call); \
+    } while (0)
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool dtype_ok(int32_t d) { return d == IKBO_F32 || d == IKBO_BF16; }
+
+size_t esize(int32_t d) { return d == IKBO_F32 ? 4 : 2; }
+
+// Sequential carve-out of a caller workspace.
+struct Carver {
+    char *base;
+    size_t used = 0;
+    explicit Carver(void *b) : base((char *)b) {}
+    void *take(size_t bytes) {
+        void *p = base ? base + used : nullptr;
+        used += align256(bytes);
+        return p;
+    }
+};
+
+// ---- DCA ----------------------------------------------------------------------------------------
+size_t dca_ws(int64_t C, int64_t R, Carver *c, int32_t **counts, int32_t **off, int32_t **tiles, int32_t **perm) {
+    Carver local(nullptr);
+    Carver &cv = c ? *c : local;
+    int32_t *a = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(R + 1));
+    int32_t *b = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(R + 1));
+    int32_t *t = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(R + 1));
+    int32_t *p = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
+    if (counts) *counts = a;
+    if (off) *off = b;
+    if (tiles) *tiles = t;
+    if (perm) *perm = p;
+    return cv.used;
+}
+
+// ---- LCB ----------------------------------------------------------------------------------------
+int32_t lcb_splits(int64_t R, int32_t n_total, int32_t k_req, int32_t in_dtype) {
+    return ikbo::request_gemm_splits(R, n_total, k_req, in_dtype == IKBO_F32);
+}
+
+struct LcbWs {
+    int32_t *map = nullptr;
+    float *z = nullptr;
+    float *partial = nullptr;
+    size_t partial_cap = 0;   // floats
+};
+
+size_t lcb_ws(int64_t C, int64_t R, int32_t k_req, int32_t n_req, int32_t n_cand, int32_t in_dtype, Carver *c,
+              LcbWs *w, bool with_map = true) {
+    Carver local(nullptr);
+    Carver &cv = c ? *c : local;
+    const int32_t n_total = n_req + n_cand;
+    int32_t s = 1;
+    if (in_dtype < 0) {  // size for either dtype
+        s = lcb_splits(R, n_total, k_req, IKBO_F32);
+        int32_t s2 = lcb_splits(R, n_total, k_req, IKBO_BF16);
+        if (s2 > s) s = s2;
+    } else {
+        s = lcb_splits(R, n_total, k_req, in_dtype);
+    }
+    int32_t *map = with_map ? (int32_t *)cv.take(sizeof(int32_t) * (size_t)(C > 0 ? C : 1)) : nullptr;
+    float *z = (float *)cv.take(sizeof(float) * (size_t)(R > 0 ? R : 1) * (size_t)(n_cand > 0 ? n_cand : 1));
+    float *part = (float *)cv.take(sizeof(float) * (size_t)s * (size_t)(R > 0 ? R : 1) * (size_t)(n_total > 0 ? n_total : 1));
+    if (w) {
+        w->map = map;
+        w->z = z;
+        w->partial = part;
+        w->partial_cap = (size_t)s * (size_t)(R > 0 ? R : 1) * (size_t)(n_total > 0 ? n_total : 1);
+    }
+    return cv.used;
+}
+
+// One GLM layer (request GEMM + candidate GEMM with the fused gather epilogue).
+int run_lcb(const void *x_req, int64_t R, int32_t k_req, const void *x_cand, int64_t C, int32_t k_cand,
+            const int32_t *map, const void *w_rr, const void *w_cr, const void *w_cc, const float *b_r,
+            const float *b_c, int32_t n_req, int32_t n_cand, int32_t act, int32_t in_dtype, int32_t out_dtype,
+            void *y_req, void *y_cand, const LcbWs &ws, hipStream_t s) {
+    const int in_f32 = in_dtype == IKBO_F32;
+    const bool want_req = y_req != nullptr && n_req > 0;
+    // request-batched GEMM: [Y_r | Z] = x_r [W_RR ; W_CR]^T (Sec. 4.1), split-K + fixed-order reduce
+    if (R > 0 && (want_req || n_cand > 0)) {
+        ikbo::GemmArgs g = {};
+        g.x = x_req;
+        g.M = R;
+        g.K = k_req;
+        g.ldx = k_req;
+        g.w0 = want_req ? w_rr : w_cr;
+        g.w1 = w_cr;
+        g.n0 = want_req ? n_req : n_cand;
+        g.N = (want_req ? n_req : 0) + n_cand;
+        g.in_f32 = in_f32;
+        g.partial = ws.partial;
+        g.splits = lcb_splits(R, g.N, k_req, in_dtype);
+        while (g.splits > 1 && (size_t)g.splits * (size_t)R * (size_t)g.N > ws.partial_cap) --g.splits;
+        if ((size_t)R * (size_t)g.N > ws.partial_cap)
+            return fail(IKBO_WORKSPACE_TOO_SMALL, "internal: request GEMM partials exceed the workspace sizing");
+        IKBO_HIP(ikbo::launch_gemm(g, s));
+        IKBO_HIP(ikbo::launch_splitk_reduce(ws.partial, g.splits, R, g.N, want_req ? n_req : 0, b_r, act, y_req,
+                                            out_dtype == IKBO_F32, ws.z, s));
+    }
+    // candidate GEMM with the broadcast-add fused in the epilogue (Sec. 4.2.1, Eq. 14)
+    if (C > 0 && n_cand > 0) {
+        ikbo::GemmArgs g = {};
+        g.x = x_cand;
+        g.M = C;
+        g.K = k_cand;
+        g.ldx = k_cand;
+        g.w0 = w_cc;
+        g.w1 = w_cc;
+        g.n0 = n_cand;
+        g.N = n_cand;
+        g.in_f32 = in_f32;
+        g.bias = b_c;
+        g.z = ws.z;
+        g.ldz = n_cand;
+        g.map = map;
+        g.R = R;
+        g.out = y_cand;
+        g.ldo = n_cand;
+        g.out_f32 = out_dtype == IKBO_F32;
+        g.act = act;
+        g.partial = nullptr;
+        g.splits = 1;
+        IKBO_HIP(ikbo::launch_gemm(g, s));
+    }
+    return IKBO_OK;
+}
+
+int check_index_args(const int32_t *m, const int32_t *off, uint32_t flags, int64_t C) {
+    if (!m && !off && C > 0) return fail(IKBO_INVALID_ARGUMENT, "need cand_to_req or req_cand_offsets (both are NULL)");
+    if (flags & ~IKBO_INDEX_SORTED) return fail(IKBO_INVALID_ARGUMENT, "unknown index_flags bits 0x%x", flags);
+    if ((m && !aligned16(m)) || (off && !aligned16(off)))
+        return fail(IKBO_MISALIGNED, "index arrays must be 16-byte aligned");
+    return IKBO_OK;
+}
+
+int check_layer_dims(int32_t k_req, int32_t k_cand, int32_t n_req, int32_t n_cand, int32_t act, int32_t in_dtype) {
+    if (k_req < 0 || k_cand < 0 || n_req < 0 || n_cand < 0)
+        return fail(IKBO_INVALID_ARGUMENT, "negative layer width (k_req %d k_cand %d n_req %d n_cand %d)", k_req, k_cand,
+                    n_req, n_cand);
+    if (act != IKBO_ACT_NONE && act != IKBO_ACT_GELU) return fail(IKBO_INVALID_ARGUMENT, "unknown activation %d", act);
+    const int vec = in_dtype == IKBO_F32 ? 4 : 8;
+    if (k_req % vec || k_cand % vec)
+        return fail(IKBO_MISALIGNED, "k_req %d / k_cand %d must be multiples of %d (zero-pad the inputs and weights)",
+                    k_req, k_cand, vec);
+    return IKBO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ikbo_version(void) { return IKBO_VERSION; }
+
+const char *ikbo_status_string(int status) {
+    switch (status) {
+    case IKBO_OK: return "IKBO_OK";
+    case IKBO_INVALID_ARGUMENT: return "IKBO_INVALID_ARGUMENT";
+    case IKBO_UNSUPPORTED: return "IKBO_UNSUPPORTED";
+    case IKBO_MISALIGNED: return "IKBO_MISALIGNED";
+    case IKBO_WORKSPACE_TOO_SMALL: return "IKBO_WORKSPACE_TOO_SMALL";
+    case IKBO_HIP_ERROR: return "IKBO_HIP_ERROR";
+    default: return "IKBO_UNKNOWN_STATUS";
+    }
+}
+
+const char *ikbo_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t ikbo_dca_workspace_size(int64_t num_cand, int64_t num_req) {
+    if (num_cand < 0 || num_req < 0) return 0;
+    return dca_ws(num_cand, num_req, nullptr, nullptr, nullptr, nullptr, nullptr);
+}
+
+int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len, const void *k, const void *v, int64_t num_req,
+                     const int32_t *kv_cu_seqlens, int32_t kv_len, const int32_t *cand_to_req,
+                     const int32_t *req_cand_offsets, uint32_t index_flags, int32_t num_heads, int32_t head_dim,
+                     float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out, void *workspace,
+                     size_t workspace_bytes, void *hip_stream) {
+    const int64_t C = num_cand, R = num_req;
+    if (C < 0 || R < 0 || q_len <= 0 || num_heads <= 0 || head_dim <= 0 || kv_len < 0)
+        return fail(IKBO_INVALID_ARGUMENT, "bad sizes (num_cand %lld num_req %lld q_len %d heads %d head_dim %d kv_len %d)",
+                    (long long)C, (long long)R, q_len, num_heads, head_dim, kv_len);
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(IKBO_UNSUPPORTED, "dtype in %d out %d", in_dtype, out_dtype);
+    if (in_dtype == IKBO_BF16 && head_dim != 64 && head_dim != 128)
+        return fail(IKBO_UNSUPPORTED, "bf16 DCA is built for head_dim 64 and 128, got %d", head_dim);
+    if (in_dtype == IKBO_F32 && (head_dim % 4 || head_dim > 128))
+        return fail(IKBO_UNSUPPORTED, "fp32 DCA needs head_dim a multiple of 4 up to 128, got %d", head_dim);
+    int rc = check_index_args(cand_to_req, req_cand_offsets, index_flags, C);
+    if (rc) return rc;
+    if (C > 0 && (!q || !out)) return fail(IKBO_INVALID_ARGUMENT, "q and out must be non-NULL when num_cand > 0");
+    if (R > 0 && (!k || !v)) return fail(IKBO_INVALID_ARGUMENT, "k and v must be non-NULL when num_req > 0");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(kv_cu_seqlens) ||
+        !aligned16(workspace))
+        return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    if (C * (int64_t)q_len > 0x7fffffffLL || C > 0x7fffffffLL || R > 0x7ffffffeLL)
+        return fail(IKBO_UNSUPPORTED, "num_cand * q_len must fit in int32");
+    const size_t need = ikbo_dca_workspace_size(C, R);
+    if (workspace_bytes < need || (!workspace && need > 0))
+        return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (C == 0) return ok();
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int in_f32 = in_dtype == IKBO_F32;
+    const int64_t row_elems = (int64_t)q_len * num_heads * head_dim;
+    const int ob = (int)esize(out_dtype);
+
+    Carver cv(workspace);
+    int32_t *counts, *off, *tiles, *perm;
+    dca_ws(C, R, &cv, &counts, &off, &tiles, &perm);
+    const int32_t bm = ikbo::dca_block_m(head_dim, in_f32);
+    const int32_t *perm_used = nullptr;
+    if (req_cand_offsets) {
+        IKBO_HIP(ikbo::launch_scan_tiles(nullptr, req_cand_offsets, R, C, q_len, num_heads, bm, off, nullptr, tiles, s));
+        IKBO_HIP(ikbo::launch_zero_uncovered(req_cand_offsets, R, C, out, row_elems, ob, s));
+    } else {
+        // group an arbitrary map: histogram -> scan -> scatter (the scan leaves the cursor in counts)
+        IKBO_HIP(ikbo::launch_fill_i32(counts, R + 1, 0, s));
+        IKBO_HIP(ikbo::launch_histogram(cand_to_req, C, R, counts, s));
+        IKBO_HIP(ikbo::launch_scan_tiles(counts, nullptr, R, C, q_len, num_heads, bm, off, counts, tiles, s));
+        IKBO_HIP(ikbo::launch_scatter(cand_to_req, C, R, counts, perm, out, row_elems, ob, s));
+        perm_used = perm;
+    }
+    if (R == 0) return ok();
+    ikbo::DcaArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.C = C;
+    a.R = R;
+    a.Lq = q_len;
+    a.H = num_heads;
+    a.D = head_dim;
+    a.L = kv_cu_seqlens ? 0 : kv_len;
+    a.kv_cu = kv_cu_seqlens;
+    a.off = off;
+    a.perm = perm_used;
+    a.tile_start = tiles;
+    a.grid_tiles = (int64_t)num_heads * ((C * q_len) / bm + R + 1);
+    a.scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
+    a.in_f32 = in_f32;
+    a.out_f32 = out_dtype == IKBO_F32;
+    IKBO_HIP(ikbo::launch_dca(a, s));
+    return ok();
+}
+
+size_t ikbo_lcb_workspace_size(int64_t num_cand, int64_t num_req, int32_t k_req, int32_t n_req_out,
+                               int32_t n_cand_out) {
+    if (num_cand < 0 || num_req < 0 || k_req < 0 || n_req_out < 0 || n_cand_out < 0) return 0;
+    return lcb_ws(num_cand, num_req, k_req, n_req_out, n_cand_out, -1, nullptr, nullptr);
+}
+
+int ikbo_lcb_forward(const void *x_req, int64_t num_req, int32_t k_req, const void *x_cand, int64_t num_cand,
+                     int32_t k_cand, const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                     const void *w_rr, const void *w_cr, const void *w_cc, const float *b_r, const float *b_c,
+                     int32_t n_req_out, int32_t n_cand_out, int32_t activation, int32_t in_dtype, int32_t out_dtype,
+                     void *y_req, void *y_cand, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    const int64_t C = num_cand, R = num_req;
+    if (C < 0 || R < 0) return fail(IKBO_INVALID_ARGUMENT, "negative num_cand / num_req");
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(IKBO_UNSUPPORTED, "dtype in %d out %d", in_dtype, out_dtype);
+    int rc = check_layer_dims(k_req, k_cand, n_req_out, n_cand_out, activation, in_dtype);
+    if (rc) return rc;
+    rc = check_index_args(cand_to_req, req_cand_offsets, index_flags, C);
+    if (rc) return rc;
+    if (R > 0 && k_req > 0 && !x_req) return fail(IKBO_INVALID_ARGUMENT, "x_req is NULL");
+    if (C > 0 && k_cand > 0 && !x_cand) return fail(IKBO_INVALID_ARGUMENT, "x_cand is NULL");
+    if (C > 0 && n_cand_out > 0 && !y_cand) return fail(IKBO_INVALID_ARGUMENT, "y_cand is NULL");
+    if (n_cand_out > 0 && ((k_req > 0 && !w_cr) || (k_cand > 0 && !w_cc)))
+        return fail(IKBO_INVALID_ARGUMENT, "w_cr / w_cc is NULL");
+    if (y_req && n_req_out > 0 && k_req > 0 && !w_rr) return fail(IKBO_INVALID_ARGUMENT, "w_rr is NULL");
+    const void *ptrs[] = {x_req, x_cand, w_rr, w_cr, w_cc, b_r, b_c, y_req, y_cand, workspace};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    const size_t need = ikbo_lcb_workspace_size(C, R, k_req, n_req_out, n_cand_out);
+    if (workspace_bytes < need || !workspace) return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    hipStream_t s = (hipStream_t)hip_stream;
+    Carver cv(workspace);
+    LcbWs ws;
+    lcb_ws(C, R, k_req, n_req_out, n_cand_out, -1, &cv, &ws);
+    const int32_t *map = cand_to_req;
+    if (!map) {
+        IKBO_HIP(ikbo::launch_offsets_to_map(req_cand_offsets, R, C, ws.map, s));
+        map = ws.map;
+    }
+    rc = run_lcb(x_req, R, k_req, x_cand, C, k_cand, map, w_rr, w_cr, w_cc, b_r, b_c, n_req_out, n_cand_out, activation,
+                 in_dtype, out_dtype, y_req, y_cand, ws, s);
+    return rc ? rc : ok();
+}
+
+size_t ikbo_glm_mlp_workspace_size(int64_t num_cand, int64_t num_req, int32_t num_layers, const ikbo_glm_layer *layers,
+                                   int32_t in_dtype) {
+    if (num_cand < 0 || num_req < 0 || num_layers <= 0 || !layers || !dtype_ok(in_dtype)) return 0;
+    int32_t max_kr = 0, max_nr = 0, max_nc = 0, max_ntot = 0;
+    for (int l = 0; l < num_layers; ++l) {
+        const ikbo_glm_layer &ly = layers[l];
+        if (ly.k_req > max_kr) max_kr = ly.k_req;
+        if (ly.n_req_out > max_nr) max_nr = ly.n_req_out;
+        if (ly.n_cand_out > max_nc) max_nc = ly.n_cand_out;
+        if (ly.n_req_out + ly.n_cand_out > max_ntot) max_ntot = ly.n_req_out + ly.n_cand_out;
+    }
+    Carver cv(nullptr);
+    // map, Z and partials sized for the widest layer (split counts checked per layer at run time)
+    int32_t smax = 1;
+    for (int l = 0; l < num_layers; ++l) {
+        int32_t sl = lcb_splits(num_req, layers[l].n_req_out + layers[l].n_cand_out, layers[l].k_req, in_dtype);
+        if (sl > smax) smax = sl;
+    }
+    cv.take(sizeof(int32_t) * (size_t)(num_cand > 0 ? num_cand : 1));
+    cv.take(sizeof(float) * (size_t)(num_req > 0 ? num_req : 1) * (size_t)(max_nc > 0 ? max_nc : 1));
+    cv.take(sizeof(float) * (size_t)smax * (size_t)(num_req > 0 ? num_req : 1) * (size_t)(max_ntot > 0 ? max_ntot : 1));
+    if (num_layers > 1) {
+        const size_t e = esize(in_dtype);
+        for (int b = 0; b < 2; ++b) {
+            cv.take(e * (size_t)(num_req > 0 ? num_req : 1) * (size_t)(max_nr > 0 ? max_nr : 1));
+            cv.take(e * (size_t)(num_cand > 0 ? num_cand : 1) * (size_t)(max_nc > 0 ? max_nc : 1));
+        }
+    }
+    return cv.used;
+}
+
+int ikbo_glm_mlp_forward(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
+                         const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                         int32_t num_layers, const ikbo_glm_layer *layers, int32_t in_dtype, int32_t out_dtype,
+                         void *y_req, void *y_cand, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    const int64_t C = num_cand, R = num_req;
+    if (C < 0 || R < 0) return fail(IKBO_INVALID_ARGUMENT, "negative num_cand / num_req");
+    if (num_layers <= 0 || !layers) return fail(IKBO_INVALID_ARGUMENT, "need num_layers >= 1 and a host layer array");
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(IKBO_UNSUPPORTED, "dtype in %d out %d", in_dtype, out_dtype);
+    int rc = check_index_args(cand_to_req, req_cand_offsets, index_flags, C);
+    if (rc) return rc;
+    for (int l = 0; l < num_layers; ++l) {
+        const ikbo_glm_layer &ly = layers[l];
+        rc = check_layer_dims(ly.k_req, ly.k_cand, ly.n_req_out, ly.n_cand_out, ly.activation, in_dtype);
+        if (rc) return fail(rc, "layer %d: %s", l, g_last_error.c_str());
+        if (l > 0 && (ly.k_req != layers[l - 1].n_req_out || ly.k_cand != layers[l - 1].n_cand_out))
+            return fail(IKBO_INVALID_ARGUMENT, "layer %d input widths (%d, %d) do not match layer %d outputs (%d, %d)", l,
+                        ly.k_req, ly.k_cand, l - 1, layers[l - 1].n_req_out, layers[l - 1].n_cand_out);
+        if (l + 1 < num_layers && ((ly.n_req_out % (in_dtype == IKBO_F32 ? 4 : 8)) || (ly.n_cand_out % (in_dtype == IKBO_F32 ? 4 : 8))))
+            return fail(IKBO_MISALIGNED, "layer %d hidden widths must be multiples of 8 (bf16) / 4 (fp32)", l);
+        const void *ptrs[] = {ly.w_rr, ly.w_cr, ly.w_cc, ly.b_r, ly.b_c};
+        for (const void *p : ptrs)
+            if (!aligned16(p)) return fail(IKBO_MISALIGNED, "layer %d: weight pointers must be 16-byte aligned", l);
+        if ((ly.n_cand_out > 0 && ((ly.k_req > 0 && !ly.w_cr) || (ly.k_cand > 0 && !ly.w_cc))) ||
+            (ly.n_req_out > 0 && ly.k_req > 0 && !ly.w_rr))
+            return fail(IKBO_INVALID_ARGUMENT, "layer %d: NULL weight", l);
+    }
+    const ikbo_glm_layer &last = layers[num_layers - 1];
+    if (C > 0 && last.n_cand_out > 0 && !y_cand) return fail(IKBO_INVALID_ARGUMENT, "y_cand is NULL");
+    if ((R > 0 && layers[0].k_req > 0 && !x_req) || (C > 0 && layers[0].k_cand > 0 && !x_cand))
+        return fail(IKBO_INVALID_ARGUMENT, "x_req / x_cand is NULL");
+    const void *ptrs[] = {x_req, x_cand, y_req, y_cand, workspace};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    const size_t need = ikbo_glm_mlp_workspace_size(C, R, num_layers, layers, in_dtype);
+    if (workspace_bytes < need || !workspace)
+        return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+
+    hipStream_t s = (hipStream_t)hip_stream;
+    int32_t max_nr = 0, max_nc = 0, max_ntot = 0, smax = 1;
+    for (int l = 0; l < num_layers; ++l) {
+        if (layers[l].n_req_out > max_nr) max_nr = layers[l].n_req_out;
+        if (layers[l].n_cand_out > max_nc) max_nc = layers[l].n_cand_out;
+        if (layers[l].n_req_out + layers[l].n_cand_out > max_ntot) max_ntot = layers[l].n_req_out + layers[l].n_cand_out;
+        int32_t sl = lcb_splits(R, layers[l].n_req_out + layers[l].n_cand_out, layers[l].k_req, in_dtype);
+        if (sl > smax) smax = sl;
+    }
+    Carver cv(workspace);
+    LcbWs ws;
+    ws.map = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
+    ws.z = (float *)cv.take(sizeof(float) * (size_t)(R > 0 ? R : 1) * (size_t)(max_nc > 0 ? max_nc : 1));
+    ws.partial_cap = (size_t)smax * (size_t)(R > 0 ? R : 1) * (size_t)(max_ntot > 0 ? max_ntot : 1);
+    ws.partial = (float *)cv.take(sizeof(float) * ws.partial_cap);
+    void *hr[2] = {nullptr, nullptr}, *hc[2] = {nullptr, nullptr};
+    const size_t e = esize(in_dtype);
+    if (num_layers > 1)
+        for (int b = 0; b < 2; ++b) {
+            hr[b] = cv.take(e * (size_t)(R > 0 ? R : 1) * (size_t)(max_nr > 0 ? max_nr : 1));
+            hc[b] = cv.take(e * (size_t)(C > 0 ? C : 1) * (size_t)(max_nc > 0 ? max_nc : 1));
+        }
+    const int32_t *map = cand_to_req;
+    if (!map) {
+        IKBO_HIP(ikbo::launch_offsets_to_map(req_cand_offsets, R, C, ws.map, s));
+        map = ws.map;
+    }
+    const void *xr = x_req, *xc = x_cand;
+    for (int l = 0; l < num_layers; ++l) {
+        const ikbo_glm_layer &ly = layers[l];
+        const bool is_last = l + 1 == num_layers;
+        void *yr = is_last ? y_req : hr[l & 1];
+        void *yc = is_last ? y_cand : hc[l & 1];
+        rc = run_lcb(xr, R, ly.k_req, xc, C, ly.k_cand, map, ly.w_rr, ly.w_cr, ly.w_cc, ly.b_r, ly.b_c, ly.n_req_out,
+                     ly.n_cand_out, ly.activation, in_dtype, is_last ? out_dtype : in_dtype, yr, yc, ws, s);
+        if (rc) return rc;
+        xr = yr;
+        xc = yc;
+    }
+    return ok();
+}
+
+int ikbo_check_index(const int32_t *cand_to_req, const int32_t *req_cand_offsets, int64_t num_cand, int64_t num_req,
+                     uint32_t index_flags, uint64_t *d_violations, void *hip_stream) {
+    if (num_cand < 0 || num_req < 0) return fail(IKBO_INVALID_ARGUMENT, "negative sizes");
+    if (!d_violations) return fail(IKBO_INVALID_ARGUMENT, "d_violations is NULL");
+    int rc = check_index_args(cand_to_req, req_cand_offsets, index_flags, 1);
+    if (rc) return rc;
+    if (((uintptr_t)d_violations & 7u) != 0) return fail(IKBO_MISALIGNED, "d_violations must be 8-byte aligned");
+    IKBO_HIP(ikbo::launch_check_index(cand_to_req, req_cand_offsets, num_cand, num_req, index_flags, d_violations,
+                                      (hipStream_t)hip_stream));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Host-side launch entry points of the IKBO kernels (internal to libikbo; not the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ikbo {
+
+// ---- index prologue (ikbo_index.hip) ----------------------------------------------------------
+// Fill n int32 with a value (a kernel, not hipMemsetAsync, so it is safe under graph capture).
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s);
+// counts[r] += 1 for every candidate with 0 <= m[c] < R.
+hipError_t launch_histogram(const int32_t *m, int64_t C, int64_t R, int32_t *counts, hipStream_t s);
+// From counts (counts != null) or from offsets: writes off_out[0..R] (exclusive scan of counts, or a
+// sanitised copy of the offsets), cursor[0..R) = off_out[r] (may be null), and
+// tile_start[0..R] = prefix of H * ceil(rows_r / block_m) with rows_r = candidates_r * q_len.
+hipError_t launch_scan_tiles(const int32_t *counts, const int32_t *off_in, int64_t R, int64_t C, int32_t q_len,
+                             int32_t heads, int32_t block_m, int32_t *off_out, int32_t *cursor,
+                             int32_t *tile_start, hipStream_t s);
+// perm[cursor[m[c]]++] = c for valid m; rows of candidates with invalid m are zeroed in `out`
+// (row width row_elems, element size out_bytes).
+hipError_t launch_scatter(const int32_t *m, int64_t C, int64_t R, int32_t *cursor, int32_t *perm, void *out,
+                          int64_t row_elems, int out_bytes, hipStream_t s);
+// m_out[c] = r with off[r] <= c < off[r+1] (binary search over a sanitised view), -1 when none.
+hipError_t launch_offsets_to_map(const int32_t *off, int64_t R, int64_t C, int32_t *m_out, hipStream_t s);
+// Zero rows of `out` for candidates outside [clamp(off[0]), clamp(off[R])).
+hipError_t launch_zero_uncovered(const int32_t *off, int64_t R, int64_t C, void *out, int64_t row_elems,
+                                 int out_bytes, hipStream_t s);
+hipError_t launch_check_index(const int32_t *m, const int32_t *off, int64_t C, int64_t R, uint32_t flags,
+                              uint64_t *d_count, hipStream_t s);
+
+// ---- IKBO-DCA (ikbo_dca.hip) -----------------------------------------------------------------
+struct DcaArgs {
+    const void *q, *k, *v;
+    void *out;
+    int64_t C, R;
+    int32_t Lq, H, D, L;
+    const int32_t *kv_cu;       // [R+1] or null (uniform L)
+    const int32_t *off;         // [R+1] grouping (sanitised)
+    const int32_t *perm;        // [C] or null (identity)
+    const int32_t *tile_start;  // [R+1], tile_start[R] = number of tiles
+    int64_t grid_tiles;         // upper bound on tile_start[R], sizes the grid
+    float scale;
+    int32_t in_f32, out_f32;
+};
+// Rows of stacked candidate queries covered by one DCA work tile, per path.
+int32_t dca_block_m(int32_t D, int in_f32);
+hipError_t launch_dca(const DcaArgs &a, hipStream_t s);
+
+// ---- GEMMs for IKBO-LCB (ikbo_gemm.hip) ------------------------------------------------------
+struct GemmArgs {
+    const void *x;              // activations [M, K], row stride ldx elements
+    int64_t M;
+    int32_t K;
+    int64_t ldx;
+    const void *w0, *w1;        // weight rows n < n0 from w0 (row n), else from w1 (row n - n0); K contiguous
+    int32_t n0, N;
+    int32_t in_f32;
+    // direct epilogue: out[m, n] = act(acc + bias[n] + (z ? z[map[m], n] : 0)); rows whose map is
+    // outside [0, R) are written as zeros when z is set
+    const float *bias;
+    const float *z;
+    int64_t ldz;
+    const int32_t *map;
+    int64_t R;
+    void *out;
+    int64_t ldo;
+    int32_t out_f32, act;
+    // split-K: when partial != null the kernel writes fp32 partial sums [split][M][N] instead
+    float *partial;
+    int32_t splits;
+};
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+// Sum the split-K partials in a fixed order, then columns n < n_split go to out0 = act(sum + bias0)
+// ([M, n_split], out dtype) and columns n >= n_split go to out1 = sum (fp32, [M, N - n_split]).
+hipError_t launch_splitk_reduce(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
+                                const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1,
+                                hipStream_t s);
+// Split count the request GEMM uses for an M x N x K problem.
+int32_t request_gemm_splits(int64_t M, int32_t N, int32_t K, int in_f32);
+
+}  // namespace ikbo

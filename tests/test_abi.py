@@ -1,0 +1,153 @@
+"""The C ABI library: it loads, exports every symbol include/ikbo.h declares, and rejects bad
+arguments before touching the GPU. Runs without a GPU: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import request_candidate_broadcast_amd as ikbo
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ikbo.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ikbo.LIB_PATH):
+        from request_candidate_broadcast_amd import _build
+        _build.build(verbose=False)
+    return ikbo.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ikbo_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("ikbo_dca_forward", "ikbo_lcb_forward", "ikbo_glm_mlp_forward", "ikbo_check_index",
+              "ikbo_dca_workspace_size", "ikbo_lcb_workspace_size", "ikbo_glm_mlp_workspace_size",
+              "ikbo_status_string", "ikbo_last_error_message", "ikbo_version"):
+        assert n in names
+    assert sorted(ikbo.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", ikbo.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    exported = set(re.findall(r"\bT (ikbo_[a-z_0-9]+)\b", out))
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ikbo_version() == 100
+    assert lib.ikbo_status_string(0) == b"IKBO_OK"
+    assert lib.ikbo_status_string(4) == b"IKBO_WORKSPACE_TOO_SMALL"
+    assert lib.ikbo_status_string(99) == b"IKBO_UNKNOWN_STATUS"
+
+
+def test_workspace_sizes(lib):
+    assert lib.ikbo_dca_workspace_size(1000, 10) >= 4 * (1000 + 3 * 11)
+    assert lib.ikbo_dca_workspace_size(-1, 10) == 0
+    # Z in fp32 [R, N_c] at least
+    assert lib.ikbo_lcb_workspace_size(100, 8, 64, 32, 48) >= 4 * 8 * 48
+    layers = (ikbo.GlmLayer * 2)()
+    layers[0] = ikbo.GlmLayer(None, None, None, None, None, 64, 32, 48, 40, 1)
+    layers[1] = ikbo.GlmLayer(None, None, None, None, None, 48, 40, 16, 24, 0)
+    n = lib.ikbo_glm_mlp_workspace_size(100, 8, 2, layers, 1)
+    assert n >= 2 * 2 * 100 * 40      # two bf16 hidden candidate buffers
+
+
+FAKE = 0x10000          # a 16-byte-aligned address that is never dereferenced: calls fail first
+MIS = 0x10008           # 8-byte aligned only
+
+
+def dca(lib, **kw):
+    a = dict(q=FAKE, C=64, Lq=1, k=FAKE, v=FAKE, R=4, cu=None, L=16, m=FAKE, off=None, flags=0, H=2, d=128,
+             scale=0.0, ind=1, outd=0, out=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.ikbo_dca_forward(a["q"], a["C"], a["Lq"], a["k"], a["v"], a["R"], a["cu"], a["L"], a["m"], a["off"],
+                                a["flags"], a["H"], a["d"], a["scale"], a["ind"], a["outd"], a["out"], a["ws"],
+                                a["wsb"], a["stream"])
+
+
+def test_dca_argument_errors(lib):
+    assert dca(lib, m=None, off=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert b"cand_to_req" in lib.ikbo_last_error_message()
+    assert dca(lib, C=-1) == ikbo.IKBO_INVALID_ARGUMENT
+    assert dca(lib, H=0) == ikbo.IKBO_INVALID_ARGUMENT
+    assert dca(lib, flags=4) == ikbo.IKBO_INVALID_ARGUMENT
+    assert dca(lib, d=96) == ikbo.IKBO_UNSUPPORTED
+    assert dca(lib, ind=0, d=130) == ikbo.IKBO_UNSUPPORTED
+    assert dca(lib, ind=7) == ikbo.IKBO_UNSUPPORTED
+    assert dca(lib, q=MIS) == ikbo.IKBO_MISALIGNED
+    assert dca(lib, m=MIS) == ikbo.IKBO_MISALIGNED
+    assert dca(lib, q=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert dca(lib, wsb=16) == ikbo.IKBO_WORKSPACE_TOO_SMALL
+    assert dca(lib, ws=None, wsb=1 << 30) == ikbo.IKBO_WORKSPACE_TOO_SMALL
+    # nothing to do: succeeds without any GPU work
+    assert dca(lib, C=0) == ikbo.IKBO_OK
+
+
+def lcb(lib, **kw):
+    a = dict(xr=FAKE, R=4, kr=64, xc=FAKE, C=32, kc=64, m=FAKE, off=None, flags=0, wrr=FAKE, wcr=FAKE, wcc=FAKE,
+             br=None, bc=None, nr=32, nc=32, act=0, ind=1, outd=1, yr=FAKE, yc=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.ikbo_lcb_forward(a["xr"], a["R"], a["kr"], a["xc"], a["C"], a["kc"], a["m"], a["off"], a["flags"],
+                                a["wrr"], a["wcr"], a["wcc"], a["br"], a["bc"], a["nr"], a["nc"], a["act"], a["ind"],
+                                a["outd"], a["yr"], a["yc"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_lcb_argument_errors(lib):
+    assert lcb(lib, m=None, off=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcb(lib, kr=60) == ikbo.IKBO_MISALIGNED          # bf16 rows must be 16-byte multiples
+    assert lcb(lib, ind=0, kr=62) == ikbo.IKBO_MISALIGNED   # fp32: multiples of 4 elements
+    assert lcb(lib, act=5) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcb(lib, nr=-1) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcb(lib, wcc=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcb(lib, yc=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcb(lib, xc=MIS) == ikbo.IKBO_MISALIGNED
+    assert lcb(lib, wsb=8) == ikbo.IKBO_WORKSPACE_TOO_SMALL
+    assert lcb(lib, outd=3) == ikbo.IKBO_UNSUPPORTED
+
+
+def test_glm_mlp_argument_errors(lib):
+    layers = (ikbo.GlmLayer * 2)()
+    layers[0] = ikbo.GlmLayer(FAKE, FAKE, FAKE, None, None, 64, 32, 48, 40, 1)
+    layers[1] = ikbo.GlmLayer(FAKE, FAKE, FAKE, None, None, 48, 40, 16, 24, 0)
+    f = lambda n=2, ly=layers, wsb=1 << 30, m=FAKE: lib.ikbo_glm_mlp_forward(
+        FAKE, 4, FAKE, 32, m, None, 0, n, ly, 1, 1, FAKE, FAKE, FAKE, wsb, None)
+    assert f(n=0) == ikbo.IKBO_INVALID_ARGUMENT
+    assert f(m=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert f(wsb=64) == ikbo.IKBO_WORKSPACE_TOO_SMALL
+    bad = (ikbo.GlmLayer * 2)()
+    bad[0] = layers[0]
+    bad[1] = ikbo.GlmLayer(FAKE, FAKE, FAKE, None, None, 40, 40, 16, 24, 0)   # k_req != previous n_req
+    assert f(ly=bad) == ikbo.IKBO_INVALID_ARGUMENT
+    assert b"do not match" in lib.ikbo_last_error_message()
+    odd = (ikbo.GlmLayer * 2)()
+    odd[0] = ikbo.GlmLayer(FAKE, FAKE, FAKE, None, None, 64, 32, 44, 40, 1)   # hidden width not a multiple of 8
+    odd[1] = ikbo.GlmLayer(FAKE, FAKE, FAKE, None, None, 44, 40, 16, 24, 0)
+    assert f(ly=odd) == ikbo.IKBO_MISALIGNED
+
+
+def test_check_index_argument_errors(lib):
+    assert lib.ikbo_check_index(None, None, 4, 2, 0, FAKE, None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lib.ikbo_check_index(FAKE, None, 4, 2, 0, None, None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lib.ikbo_check_index(FAKE, None, 4, 2, 0, FAKE + 4, None) == ikbo.IKBO_MISALIGNED
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("request_candidate_broadcast_amd")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            mod.load_library(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved
