@@ -38,7 +38,21 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=0, help="candidates in the oracle sample (0 = default)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="per-kernel HBM bytes measured with rocprofv3 counters, if present")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (for scaling the HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch, three launches."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 3}))
 
 
 def log(msg):
@@ -47,6 +61,9 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
               file=sys.stderr)
@@ -204,14 +221,20 @@ def main():
 
     # roofline of the dominant kernel (its own events on its stream)
     dk = per[dominant]
+    # HBM bytes per launch from rocprofv3 counters (scaled by a plain copy), valid only while the
+    # kernel source is the one the counters were taken on
     traffic = None
     try:
+        import hashlib
         with open(args.traffic_json) as f:
             tj = json.load(f)
         ent = tj.get(args.workload, {}).get(dominant)
         if ent:
-            traffic = ent.get("bytes_per_launch")
-    except (OSError, ValueError):
+            with open(os.path.join(ROOT, ent["file"]), "rb") as f:
+                sha = hashlib.sha256(f.read()).hexdigest()[:16]
+            if sha == ent.get("source_sha256_prefix"):
+                traffic = ent.get("bytes_per_launch")
+    except (OSError, ValueError, KeyError):
         traffic = None
     roofline = {"bound": "mfma", "achieved": round(dk["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(dk["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
@@ -240,7 +263,7 @@ def cpu_baseline(args, np):
     t0 = time.perf_counter()
     if args.workload == "block":
         g, s = synth.block_specs()
-        n_per = args.cpu_sample // 4 if args.cpu_sample else 8
+        n_per = args.cpu_sample // 4 if args.cpu_sample else 96
         reqs = [0, 1, g.R // 2, g.R - 1]
         off = g.offsets
         # compact inputs: the sampled candidates' rows, and the K/V blocks of their requests only

@@ -30,14 +30,12 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace ikbo {
 
 namespace {
 
-constexpr int kBlockN = 64;        // keys per LDS tile
-constexpr int kWavesBf16 = 8;      // waves per workgroup (2 per SIMD)
-constexpr int kBlockMBf16 = kWavesBf16 * 32;
-constexpr float kTau = 8.0f;       // lazy-rescale threshold, log2 units (p <= 2^8)
 
 __device__ __forceinline__ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -100,161 +98,184 @@ __device__ __forceinline__ void row_source(const DcaArgs &a, const TileInfo &ti,
 
 // ----------------------------------------------------------------------------------------------
 // bf16 inputs, D in {64, 128}, MFMA path.
-template <int D>
-__global__ __launch_bounds__(kWavesBf16 * 64) void dca_bf16_kernel(DcaArgs a) {
+//
+// Template parameters: NW waves per workgroup, NG groups of 32 query columns per wave, NKB
+// 32-key blocks per K/V tile, NBUF LDS stages, LATE = copy the next tiles in after this tile's
+// V fragments are read (else at the top of the tile). With NG = 2 the work of one tile is
+// ordered so the softmax VALU work of one group overlaps the MFMA work of the other
+// (scheduling fences keep the phases apart):
+//   A: S0 = K Q0^T                     (MFMA)
+//   B: S1 = K Q1^T        | softmax(S0) (MFMA | VALU)
+//   C: O0 += V^T P0^T     | softmax(S1)
+//   D: O1 += V^T P1^T
+// K fragments are read from LDS once per tile and used by every group, likewise the V^T
+// fragments. K/V tiles are copied global -> LDS directly (no register staging); one barrier per
+// tile.
+
+// Cross-half combine: v_permlane32_swap exchanges the two 32-lane halves, so the max (or sum) of
+// both results is the value over lanes l and l ^ 32.
+__device__ __forceinline__ float half_swap_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Thin wrappers of target builtins, so the generic lambdas of the kernel below only call
+// device functions.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// s_waitcnt with vmcnt(N) and the other counters left free (expcnt 7, lgkmcnt 15); N < 16
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { __builtin_amdgcn_s_waitcnt(0x0F70 | N); }
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
+// Masks keys at or past L_r in the last tile: s[kb][j] holds key kb*32 + 8*(j/4) + 4*half + j%4.
+template <int NKB>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[NKB], int rem, int half) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3) >= rem) s[kb][j] = -INFINITY;
+}
+
+// Max over the lane's scores of one tile, then over the two 32-lane halves (one query column).
+template <int NKB>
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[NKB]) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int j = (kb == 0 ? 2 : 0); j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+    return half_swap_max(mx);
+}
+
+// p = 2^(s * scale * log2(e) - m_ref) against a fixed per-query reference; accumulates the row
+// sum and packs the bf16 B operands of the PV MFMAs.
+template <int NKB>
+__device__ __forceinline__ void exp_tile(f32x16 (&s)[NKB], bf16x8 (&pb)[NKB][2], float &l, float cl2, float mneg) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j], cl2, mneg));
+            s[kb][j] = p;
+            l += p;
+        }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[kb][u][e] = (__bf16)s[kb][8 * u + e];
+}
+
+template <int D, int NW, int NG, int NKB, int NBUF, bool LATE>
+__global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
+    constexpr int BN = NKB * 32;                       // keys per tile
+    constexpr int BM = NW * NG * 32;                   // stacked query rows per workgroup
     constexpr int CPR = D / 8;                         // 16-byte chunks per key row
-    constexpr int kTileChunks = kBlockN * CPR;         // chunks per K (or V) tile
-    constexpr int kThreads = kWavesBf16 * 64;
+    constexpr int kTileChunks = BN * CPR;              // chunks per K (or V) tile
+    constexpr int kThreads = NW * 64;
     constexpr int kLoadPasses = kTileChunks / kThreads;
     static_assert(kTileChunks % kThreads == 0, "tile load must split evenly");
+    constexpr int kCopiesPerTile = 2 * kLoadPasses;    // global -> LDS instructions per tile (K and V)
+    static_assert(kCopiesPerTile < 16, "vmcnt immediate");
+    static_assert(NBUF == 2 || (NBUF == 3 && LATE), "three stages are filled late");
     constexpr int KS = D / 16;                         // k16 steps over the head dim
     constexpr int DB = D / 32;                         // 32-row blocks of O^T
 
-    __shared__ uint4 smem[2][2][kTileChunks];          // [stage][K=0 / V=1][chunk]
+    __shared__ uint4 smem[NBUF][2][kTileChunks];       // [stage][K=0 / V=1][chunk]
 
     TileInfo ti;
-    if (!decode_tile(a, kBlockMBf16, ti)) return;
+    if (!decode_tile(a, BM, ti)) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
     const int64_t HD = (int64_t)a.H * D;
 
-    // ---- this lane's query row (column of S^T) ----
-    const int64_t srow = ti.qb * kBlockMBf16 + wave * 32 + l32;
-    const bool rvalid = srow < ti.rows;
-    int64_t cand = 0;
-    int tok = 0;
-    if (rvalid) row_source(a, ti, srow, cand, tok);
-    bf16x8 qf[KS];
-    {
-        const uint16_t *qp = (const uint16_t *)a.q + ((cand * a.Lq + tok) * HD + ti.h * D) + half * 8;
+    // ---- the lane's query rows (one column of S^T per group) ----
+    bool rvalid[NG];
+    int64_t cand[NG];
+    int tok[NG];
+    bf16x8 qf[NG][KS];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int64_t srow = ti.qb * BM + wave * (NG * 32) + g * 32 + l32;
+        rvalid[g] = srow < ti.rows;
+        cand[g] = 0;
+        tok[g] = 0;
+        if (rvalid[g]) row_source(a, ti, srow, cand[g], tok[g]);
+        const uint16_t *qp = (const uint16_t *)a.q + ((cand[g] * a.Lq + tok[g]) * HD + ti.h * D) + half * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 u = rvalid ? *(const uint4 *)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-            qf[ks] = __builtin_bit_cast(bf16x8, u);
+            uint4 u = rvalid[g] ? *(const uint4 *)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+            qf[g][ks] = __builtin_bit_cast(bf16x8, u);
         }
     }
 
-    // ---- K/V tile loader ----
+    // ---- K/V tile copies: global -> LDS direct ----
+    // Each wave instruction fills 64 consecutive 16-byte LDS slots; the lane that fills slot
+    // (key, c') reads chunk c' ^ swizzle(key) of that key row, which realises the swizzled layout.
+    // Rows past L_r are read from row L_r - 1 instead: their scores are masked to -inf, so they
+    // get weight exactly 0 and their finite values do not matter.
     const uint16_t *kbase = (const uint16_t *)a.k + ti.kv_row0 * HD + ti.h * D;
     const uint16_t *vbase = (const uint16_t *)a.v + ti.kv_row0 * HD + ti.h * D;
-    const int64_t Lr = ti.Lr;
-    uint4 pk[kLoadPasses], pv[kLoadPasses];
-    auto gload = [&](int64_t n0) {
+    const int Lr = (int)ti.Lr;
+    auto dma = [&](int n0, int st) {
 #pragma unroll
         for (int p = 0; p < kLoadPasses; ++p) {
-            const int qd = tid + p * kThreads, key = qd / CPR, ch = qd % CPR;
-            if (n0 + key < Lr) {
-                const int64_t off = (n0 + key) * HD + ch * 8;
-                pk[p] = *(const uint4 *)(kbase + off);
-                pv[p] = *(const uint4 *)(vbase + off);
-            } else {
-                pk[p] = make_uint4(0, 0, 0, 0);
-                pv[p] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto lstore = [&](int st) {
-#pragma unroll
-        for (int p = 0; p < kLoadPasses; ++p) {
-            const int qd = tid + p * kThreads, key = qd / CPR, ch = qd % CPR;
-            smem[st][0][key * CPR + (ch ^ swz_k<D>(key))] = pk[p];
-            smem[st][1][key * CPR + (ch ^ swz_v(key))] = pv[p];
+            const int slot0 = p * kThreads + wave * 64;
+            const int slot = slot0 + lane, key = slot / CPR, chp = slot % CPR;
+            const int row = min(n0 + key, Lr - 1);
+            const int64_t roff = (int64_t)row * HD;
+            copy16_to_lds(kbase + roff + (chp ^ swz_k<D>(key)) * 8, &smem[st][0][slot0]);
+            copy16_to_lds(vbase + roff + (chp ^ swz_v(key)) * 8, &smem[st][1][slot0]);
         }
     };
 
-    f32x16 o[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[db][j] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;
     const float cl2 = a.scale * 1.4426950408889634f;
-
-    const int64_t ntiles = (Lr + kBlockN - 1) / kBlockN;
-    if (ntiles > 0) {
-        gload(0);
-        lstore(0);
-    }
-    __syncthreads();
 
     // lane constants of the transposed V read
     const int g16 = lane >> 4, s16 = lane & 15;
-    const int tr_dsub = (g16 & 1) * 16 + 4 * (s16 & 3);   // + db * 32
-    const int tr_key = 4 * (g16 >> 1) + (s16 >> 2);        // + kb * 32 + 16 u + 8 t
+    const int tr_dsub = (g16 & 1) * 16 + 4 * (s16 & 3);
+    const int tr_key = 4 * (g16 >> 1) + (s16 >> 2);
 
-    for (int64_t it = 0; it < ntiles; ++it) {
-        const int st = (int)(it & 1);
-        const int64_t n0 = it * kBlockN;
-        if (it + 1 < ntiles) gload(n0 + kBlockN);
-
-        // ---- S^T = K Q^T for 64 keys (two 32-key blocks) ----
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) s[kb][j] = 0.0f;
+    // K fragments of one tile (A operands of S^T = K Q^T)
+    auto k_frags = [&](int st, bf16x8 (&kf)[KS][NKB]) {
         const uint4 *ks_lds = smem[st][0];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb) {
                 const int key = kb * 32 + l32, ch = ks * 2 + half;
-                bf16x8 af = __builtin_bit_cast(bf16x8, ks_lds[key * CPR + (ch ^ swz_k<D>(key))]);
-                s[kb] = mfma_32x32x16_bf16(af, qf[ks], s[kb]);
+                kf[ks][kb] = __builtin_bit_cast(bf16x8, ks_lds[key * CPR + (ch ^ swz_k<D>(key))]);
             }
-        }
-
-        // ---- online softmax (exp2 domain, lazy rescale) ----
-        if (n0 + kBlockN > Lr) {
+    };
+    auto s_tile = [&](const bf16x8 (&kf)[KS][NKB], const bf16x8 (&q)[KS], f32x16 (&s)[NKB]) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int64_t key = n0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-                    if (key >= Lr) s[kb][j] = -INFINITY;
-                }
-        }
-        float mx = s[0][0];
+            for (int j = 0; j < 16; ++j) s[kb][j] = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = mx * cl2;
-        const bool need = m_new > m_run + kTau;
-        if (__any(need)) {
-            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-            if (need) m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-        }
-        bf16x8 pb[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j], cl2, -m_run));
-                s[kb][j] = p;
-                l_run += p;
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pb[kb][u][e] = (__bf16)s[kb][8 * u + e];
-        }
-
-        // ---- O^T += V^T P^T ----
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma_32x32x16_bf16(kf[ks][kb], q[ks], s[kb]);
+    };
+    // V^T fragments of one tile (A operands of O^T += V^T P^T) through the transposing LDS read
+    auto v_frags = [&](int st, bf16x8 (&vf)[DB][NKB][2]) {
         const char *vs_lds = (const char *)smem[st][1];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const int dcol = db * 32 + tr_dsub;
             const int chunk = dcol >> 3, sub = (dcol & 7) * 2;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int key0 = kb * 32 + 16 * u + tr_key;
@@ -264,34 +285,176 @@ __global__ __launch_bounds__(kWavesBf16 * 64) void dca_bf16_kernel(DcaArgs a) {
                     i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (lds_i16x4 *)(vs_lds + (key1 * CPR + (chunk ^ swz_v(key1))) * 16 + sub));
                     typedef short i16x8 __attribute__((ext_vector_type(8)));
-                    i16x8 av = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[kb][u], o[db]);
+                    vf[db][kb][u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
         }
+    };
+    auto pv_tile = [&](const bf16x8 (&vf)[DB][NKB][2], const bf16x8 (&pb)[NKB][2], f32x16 (&o)[DB]) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) o[db] = mfma_32x32x16_bf16(vf[db][kb][u], pb[kb][u], o[db]);
+    };
 
-        if (it + 1 < ntiles) lstore(st ^ 1);
+    const int ntiles = (Lr + BN - 1) / BN;
+    const bool ragged = (Lr % BN) != 0;
+
+    // ---- one pass over the keys ----
+    // Softmax weights are taken against a fixed per-query reference m_ref (no running rescale of
+    // O): O' = sum_j 2^(s_j c - m_ref) v_j and l' = sum_j 2^(s_j c - m_ref) give O = O' / l' exactly
+    // in real arithmetic for any m_ref. With INIT the reference is the max of the first tile;
+    // later tiles may exceed it, and a query whose sums overflow is redone with its true max.
+    // With MAXONLY the pass only computes scores and leaves each query's exact max in m_ref.
+    f32x16 o[NG][DB];
+    float l[NG], mref[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        l[g] = 0.0f;
+        mref[g] = 0.0f;
+    }
+    auto pass = [&](auto init, auto maxonly) {
+        constexpr bool INIT = decltype(init)::value;
+        constexpr bool MAXONLY = decltype(maxonly)::value;
+        float mx[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            l[g] = 0.0f;
+            mx[g] = -INFINITY;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[g][db][j] = 0.0f;
+        }
+        // prologue: the first tile (and with three stages the second) in flight, the first landed
+        if (ntiles > 0) dma(0, 0);
+        if (NBUF == 3 && ntiles > 1) {
+            dma(BN, 1);
+            wait_vmcnt<kCopiesPerTile>();
+        } else {
+            wait_all();
+        }
         __syncthreads();
+        auto tile = [&](int it, auto first, auto masked) {
+            constexpr bool FIRST = decltype(first)::value;
+            constexpr bool MASK = decltype(masked)::value;
+            const int st = it % NBUF;
+            const int n0 = it * BN;
+            const int ahead = it + NBUF - 1;               // the tile copied in during this one
+            const bool copy = ahead < ntiles;
+            if (!LATE && copy) dma(ahead * BN, ahead % NBUF);
+            f32x16 s[NG][NKB];
+            bf16x8 p[NG][NKB][2];
+            bf16x8 kf[KS][NKB];
+            bf16x8 vf[DB][NKB][2];
+            k_frags(st, kf);
+            auto softmax = [&](int g) {
+                if (MASK) mask_tile<NKB>(s[g], Lr - n0, half);
+                if (MAXONLY) {
+                    mx[g] = fmaxf(mx[g], tile_max<NKB>(s[g]));
+                } else {
+                    if (INIT && FIRST) mref[g] = tile_max<NKB>(s[g]) * cl2;
+                    exp_tile<NKB>(s[g], p[g], l[g], cl2, -mref[g]);
+                }
+            };
+            s_tile(kf, qf[0], s[0]);                                         // A
+            sched_fence();
+            if (NG == 2) {
+                s_tile(kf, qf[NG - 1], s[NG - 1]);                           // B
+                softmax(0);
+                sched_fence();
+            } else {
+                softmax(0);
+            }
+            if (!MAXONLY) v_frags(st, vf);
+            if (LATE && copy) dma(ahead * BN, ahead % NBUF);
+            if (!MAXONLY) {
+                pv_tile(vf, p[0], o[0]);                                     // C
+                if (NG == 2) {
+                    softmax(NG - 1);
+                    sched_fence();
+                    pv_tile(vf, p[NG - 1], o[NG - 1]);                       // D
+                }
+            } else if (NG == 2) {
+                softmax(NG - 1);
+            }
+            // the next tile must have landed; with three stages the one after may stay in flight
+            if (NBUF == 3 && it + 2 < ntiles) wait_vmcnt<kCopiesPerTile>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+        };
+        const std::true_type T;
+        const std::false_type F;
+        if (ntiles == 1) {
+            if (ragged) tile(0, T, T); else tile(0, T, F);
+        } else if (ntiles > 1) {
+            tile(0, T, F);
+            for (int it = 1; it + 1 < ntiles; ++it) tile(it, F, F);
+            if (ragged) tile(ntiles - 1, F, T); else tile(ntiles - 1, F, F);
+        }
+        if (MAXONLY) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) mref[g] = mx[g] * cl2;
+        }
+    };
+
+    pass(std::true_type(), std::false_type());
+
+    // ---- overflow check: redo the tile for the queries whose sums left the fp32 range ----
+    bool bad[NG];
+    bool any_bad = false;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        bool b = !(half_swap_sum(l[g]) < INFINITY);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) b |= !(fabsf(o[g][db][j]) < INFINITY);
+        // a query column lives in lanes l and l ^ 32: both halves must take the same decision
+        bad[g] = half_swap_max(b ? 1.0f : 0.0f) > 0.0f && rvalid[g];
+        any_bad |= bad[g];
+    }
+    if (__syncthreads_or(any_bad)) {
+        float keep[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) keep[g] = mref[g];
+        pass(std::false_type(), std::true_type());               // exact max per query
+#pragma unroll
+        for (int g = 0; g < NG; ++g) mref[g] = bad[g] ? mref[g] : keep[g];
+        pass(std::false_type(), std::false_type());              // redo; unchanged queries repeat bit for bit
     }
 
     // ---- epilogue: O = O^T / l, store rows ----
-    if (!rvalid) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int64_t obase = (cand * a.Lq + tok) * HD + ti.h * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int g = 0; g < NG; ++g) {
+        const float l_tot = half_swap_sum(l[g]);
+        if (!rvalid[g]) continue;
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        const int64_t obase = (cand[g] * a.Lq + tok[g]) * HD + ti.h * D;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int d = db * 32 + 8 * jj + 4 * half;
-            const float v0 = o[db][4 * jj + 0] * inv, v1 = o[db][4 * jj + 1] * inv;
-            const float v2 = o[db][4 * jj + 2] * inv, v3 = o[db][4 * jj + 3] * inv;
-            if (a.out_f32) {
-                *(float4 *)((float *)a.out + obase + d) = make_float4(v0, v1, v2, v3);
-            } else {
-                *(uint2 *)((uint16_t *)a.out + obase + d) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d = db * 32 + 8 * jj + 4 * half;
+                const float v0 = o[g][db][4 * jj + 0] * inv, v1 = o[g][db][4 * jj + 1] * inv;
+                const float v2 = o[g][db][4 * jj + 2] * inv, v3 = o[g][db][4 * jj + 3] * inv;
+                if (a.out_f32) {
+                    *(float4 *)((float *)a.out + obase + d) = make_float4(v0, v1, v2, v3);
+                } else {
+                    *(uint2 *)((uint16_t *)a.out + obase + d) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+                }
             }
-        }
+    }
 }
+
+// The configuration the library launches, per head dim.
+template <int D>
+struct DcaBf16Config {
+    static constexpr int NW = 4, NG = 2, NKB = 2, NBUF = 3;
+    static constexpr bool LATE = true;
+    static constexpr int BM = NW * NG * 32;
+};
 
 // ----------------------------------------------------------------------------------------------
 // fp32 inputs, any D that is a multiple of 4 up to 128. 16 query rows per workgroup, 16 lanes
@@ -383,8 +546,8 @@ __global__ __launch_bounds__(256) void dca_f32_kernel(DcaArgs a) {
 }  // namespace
 
 int32_t dca_block_m(int32_t D, int in_f32) {
-    (void)D;
-    return in_f32 ? kF32Rows : kBlockMBf16;
+    if (in_f32) return kF32Rows;
+    return D == 128 ? DcaBf16Config<128>::BM : DcaBf16Config<64>::BM;
 }
 
 hipError_t launch_dca(const DcaArgs &a, hipStream_t s) {
@@ -394,9 +557,13 @@ hipError_t launch_dca(const DcaArgs &a, hipStream_t s) {
     if (a.in_f32) {
         hipLaunchKernelGGL(dca_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
     } else if (a.D == 128) {
-        hipLaunchKernelGGL(dca_bf16_kernel<128>, dim3((unsigned)grid), dim3(kWavesBf16 * 64), 0, s, a);
+        using C = DcaBf16Config<128>;
+        hipLaunchKernelGGL((dca_bf16_kernel<128, C::NW, C::NG, C::NKB, C::NBUF, C::LATE>), dim3((unsigned)grid),
+                           dim3(C::NW * 64), 0, s, a);
     } else if (a.D == 64) {
-        hipLaunchKernelGGL(dca_bf16_kernel<64>, dim3((unsigned)grid), dim3(kWavesBf16 * 64), 0, s, a);
+        using C = DcaBf16Config<64>;
+        hipLaunchKernelGGL((dca_bf16_kernel<64, C::NW, C::NG, C::NKB, C::NBUF, C::LATE>), dim3((unsigned)grid),
+                           dim3(C::NW * 64), 0, s, a);
     } else {
         return hipErrorInvalidValue;
     }

@@ -183,3 +183,25 @@ def test_empty_inputs():
     note("dca empty")
     got = run_gpu(s, q, k, v)
     assert got.shape == (0, 1, 1, 64)
+
+
+def test_scores_far_above_the_first_tile_take_the_exact_path():
+    # Scores in a later key tile far above the first tile's max overflow the fixed-reference sums;
+    # those queries are recomputed against their exact max. Other queries of the same work tile
+    # must come out bit for bit as in a run where nothing overflows.
+    counts = [300]
+    L, H, d = 200, 1, 128
+    s, q, k, v = make_case(47, counts, [L], H, d, 1, "bf16")
+    big_q = q.copy()
+    big_k = k.copy()
+    hot = synth.f32_to_bf16_bits(np.full(d, 8.0, np.float32))
+    big_q[5, 0, 0] = hot          # candidate 5's query
+    big_k[150, 0] = hot           # key 150 (third tile): score 8*8*128/sqrt(128) ~ 724 -> 2^1045
+    note("dca exact-path fallback")
+    got = run_gpu(s, big_q, big_k, v)
+    want = oracle.dca(big_q, big_k.reshape(1, L, H, d), v.reshape(1, L, H, d), 1, m=s.cand_to_req)
+    assert_parity(down_f64(got), want, "bf16", "fallback")
+    ref = run_gpu(s, q, big_k, v)   # same keys, no hot query: nothing overflows
+    others = [c for c in range(s.C) if c != 5]
+    # queries other than 5 see the hot key too, so compare them with the run that has no hot query
+    assert torch.equal(got[others], ref[others])
