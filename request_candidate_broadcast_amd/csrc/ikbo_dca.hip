@@ -123,17 +123,6 @@ __device__ __forceinline__ float half_swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Thin wrappers of target builtins, so the generic lambdas of the kernel below only call
-// device functions.
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-// s_waitcnt with vmcnt(N) and the other counters left free (expcnt 7, lgkmcnt 15); N < 16
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() { __builtin_amdgcn_s_waitcnt(0x0F70 | N); }
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
-__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
-}
-
 // Masks keys at or past L_r in the last tile: s[kb][j] holds key kb*32 + 8*(j/4) + 4*half + j%4.
 template <int NKB>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[NKB], int rem, int half) {
@@ -185,7 +174,6 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
     constexpr int kLoadPasses = kTileChunks / kThreads;
     static_assert(kTileChunks % kThreads == 0, "tile load must split evenly");
     constexpr int kCopiesPerTile = 2 * kLoadPasses;    // global -> LDS instructions per tile (K and V)
-    static_assert(kCopiesPerTile < 16, "vmcnt immediate");
     static_assert(NBUF == 2 || (NBUF == 3 && LATE), "three stages are filled late");
     constexpr int KS = D / 16;                         // k16 steps over the head dim
     constexpr int DB = D / 32;                         // 32-row blocks of O^T

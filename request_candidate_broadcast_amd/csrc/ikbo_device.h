@@ -36,6 +36,43 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Thin wrappers of target builtins, so generic lambdas inside kernels only call device functions.
+// No instruction is moved across a scheduling fence.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// s_waitcnt vmcnt(N) leaving expcnt (7) and lgkmcnt (15) free; vmcnt is split over bits 3:0
+// and 15:14
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+// Workgroup barrier without the memory fences of __syncthreads(). Those fences make the compiler
+// wait for every load in flight (vmcnt 0), direct global -> LDS copies included, which defeats
+// copies meant to stay in flight across the barrier. Callers wait for the copies they need
+// (wait_vmcnt) before calling this; it waits for the wave's own LDS accesses (lgkmcnt 0), and the
+// asm memory clobber keeps the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");
+}
+// Direct global -> LDS copy of 16 bytes per lane: the wave's 64 lanes fill 64 consecutive 16-byte
+// LDS slots starting at lds_wave_base (taken from the first lane), lane i slot i.
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end return zero. The
+// last word is the gfx9-family default (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+// Buffer -> LDS copy of 16 bytes per lane from byte offset voff (out-of-range lanes write zeros);
+// LDS slots as in copy16_to_lds.
+__device__ __forceinline__ void buffer_copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
 // Map a hardware workgroup id to a logical tile so that each XCD works through one contiguous
 // range of logical tiles (consecutive tiles share request K/V or GEMM operands, and share an L2
 // only when they run on the same XCD). Returns -1 for ids past the end.

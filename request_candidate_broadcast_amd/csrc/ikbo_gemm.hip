@@ -8,14 +8,16 @@
 // 16-byte reads of the request-derived term Z[m[row], n..n+3], added in registers before the
 // activation and the single store. The candidate GEMM result is never written to memory on its own.
 //
-// Tile 256 x 256 x 64, 8 waves (2 along N x 4 along M, each 128 x 64), LDS double-buffered with
-// register-staged prefetch of the next k-tile. Tiles are numbered with the N tile fastest and each
+// Tile 256 x 256 x 64, 8 waves (2 along N x 4 along M, each 128 x 64), two LDS stages filled by
+// direct buffer -> LDS copies of the next k tile while the current one is multiplied. Tiles are numbered with the N tile fastest and each
 // XCD takes a contiguous range, so the N tiles that share one block of activation rows run
 // together on one XCD and read those rows through its L2.
 //
 // The request GEMM ([Y_r | Z] = x_r [W_RR; W_CR]^T, a small M = num_req) runs split-K into fp32
 // partial sums, reduced in a fixed order by a second kernel that also applies the request-group
 // epilogue; results are deterministic.
+#include <utility>
+
 #include "ikbo_device.h"
 #include "ikbo_launch.h"
 
@@ -23,16 +25,11 @@ namespace ikbo {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kGemmWaves = 8;
-constexpr int kGemmThreads = kGemmWaves * 64;
-constexpr int WM = 64, WN = 128;                 // per-wave tile (M x N)
-constexpr int MB = WM / 32, NB = WN / 32;        // 32x32 accumulator blocks per wave
-constexpr int kChunksPerRow = BK / 8;            // 16-byte chunks per tile row
-constexpr int kTileChunks = BM * kChunksPerRow;  // 2048 per operand tile
-constexpr int kLoadPasses = kTileChunks / kGemmThreads;
-
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// bf16 configuration: 4 x 2 waves, each 64 activation rows x 128 output columns, 64-deep k tiles
+// in two LDS stages
+constexpr int kWGM = 4, kWGN = 2, kTM = 64, kTN = 128;
+constexpr int BM = kWGM * kTM, BN = kWGN * kTN, BK = 64;
+constexpr int kGemmThreads = kWGM * kWGN * 64;
 
 __device__ __forceinline__ float apply_act(int act, float x) { return act == 1 ? gelu_exact(x) : x; }
 
@@ -97,11 +94,71 @@ __device__ __forceinline__ bool row_request(const GemmArgs &a, int64_t row, int6
 }
 
 // ----------------------------------------------------------------------------------------------
-template <bool PARTIAL>
-__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs a, int32_t tiles_m, int32_t tiles_n,
-                                                                 int32_t k_per_split) {
-    __shared__ uint4 sx[2][kTileChunks];
-    __shared__ uint4 sw[2][kTileChunks];
+// ----------------------------------------------------------------------------------------------
+// bf16 GEMM, templated on the wave grid (WGM along M x WGN along N), the per-wave tile (TM
+// activation rows x TN output columns, in 32x32x16 MFMA blocks), the k-tile depth TBK and the
+// number of LDS stages NBUF.
+//
+// DMA: tiles go global -> LDS directly with buffer loads (each wave instruction fills 64
+// consecutive 16-byte slots; the lane filling slot (row, c') reads chunk c' ^ swizzle(row)). This
+// needs K to be a multiple of TBK and a tile that does not straddle the w0 / w1 boundary; rows past
+// M or N fall outside the tile's buffer range and read as zeros. Otherwise the next tile is staged
+// through registers (any K that is a multiple of 8). With NBUF stages tile it + NBUF - 1 is copied
+// during tile it into the stage that tile it - 1 used, and only tile it + 1 is waited for.
+//
+// Each stage is its own LDS variable and the stage index is a compile-time constant everywhere
+// (the k loop is unrolled by NBUF): reads of one stage then carry an alias scope distinct from the
+// copies in flight into another, so the compiler does not hold them back until those land.
+// Fragments for k step ks + 1 are read into a second register set before the MFMAs of step ks.
+// LDS chunk swizzle for rows of CPR 16-byte chunks: 16 consecutive rows read at one logical chunk
+// land in 16 distinct 16-byte bank groups.
+template <int CPR>
+__device__ __forceinline__ int swzc(int row) { return CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(IC<I>{}), ...);
+}
+// f(IC<0>), f(IC<1>), ..., f(IC<N-1>)
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL>
+__global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t tiles_m, int32_t tiles_n,
+                                                            int32_t k_per_split) {
+    constexpr int T = WGM * WGN * 64;
+    constexpr int TBM = WGM * TM, TBN = WGN * TN;
+    constexpr int CPR = TBK / 8;                       // 16-byte chunks per tile row
+    constexpr int XCH = TBM * CPR, WCH = TBN * CPR;    // chunks per X / W tile
+    constexpr int XP = XCH / T, WP = WCH / T;          // load passes
+    static_assert(XCH % T == 0 && WCH % T == 0, "tile load must split evenly");
+    constexpr int MB = TM / 32, NB = TN / 32;
+    constexpr int kCopies = XP + WP;
+    static_assert(NBUF == 2 || DMA, "more than two stages need the direct copies");
+    constexpr uint32_t kOutOfRange = 0x80000000u;      // past every tile's buffer range (< 2^31 bytes)
+    static_assert(NBUF <= 4 && (NBUF - 2) * kCopies < 64, "vmcnt range");
+    static_assert(!DMA || (T / CPR) % 16 == 0, "direct copies: the chunk swizzle must repeat every pass");
+
+    // one LDS variable per stage: the compiler gives each its own alias scope, so reading one stage
+    // does not wait for copies still in flight into another
+    __shared__ uint4 sx0[XCH], sx1[XCH], sx2[NBUF > 2 ? XCH : 1], sx3[NBUF > 3 ? XCH : 1];
+    __shared__ uint4 sw0[WCH], sw1[WCH], sw2[NBUF > 2 ? WCH : 1], sw3[NBUF > 3 ? WCH : 1];
+    auto xs = [&](auto S) -> uint4 * {
+        if constexpr (decltype(S)::value == 0) return sx0;
+        else if constexpr (decltype(S)::value == 1) return sx1;
+        else if constexpr (decltype(S)::value == 2) return sx2;
+        else return sx3;
+    };
+    auto ws = [&](auto S) -> uint4 * {
+        if constexpr (decltype(S)::value == 0) return sw0;
+        else if constexpr (decltype(S)::value == 1) return sw1;
+        else if constexpr (decltype(S)::value == 2) return sw2;
+        else return sw3;
+    };
 
     const int64_t total = (int64_t)tiles_m * tiles_n * a.splits;
     int64_t t = xcd_tile(blockIdx.x, total);
@@ -110,48 +167,100 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs a, int
     t /= tiles_n;
     const int mt = (int)(t % tiles_m);
     const int sp = (int)(t / tiles_m);
-    const int64_t m0 = (int64_t)mt * BM;
-    const int n0 = nt * BN;
+    const int64_t m0 = (int64_t)mt * TBM;
+    const int n0 = nt * TBN;
     const int kbeg = sp * k_per_split;
     const int kend = min(a.K, kbeg + k_per_split);
-    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+    const int nk = kend > kbeg ? (kend - kbeg + TBK - 1) / TBK : 0;
+    // The N tiles that share a block of activation rows run side by side on one XCD. Starting each
+    // one k tile further along (nt mod 4) staggers them: one of them misses L2 on a given activation
+    // tile and the others find it there, instead of all of them waiting on the same miss.
+    const int krot = nk > 0 ? (nt & 3) % nk : 0;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
-    const int wn = wave >> 2, wm = wave & 3;
+    const int wn = wave / WGM, wm = wave % WGM;
 
-    // per-thread global source rows for the tile loads
-    const uint16_t *xrow[kLoadPasses];
-    const uint16_t *wrow[kLoadPasses];
+    // Register-staged path: source row pointers of this thread's copies (rows past M / N repeat the
+    // last valid row; their results are never stored).
+    constexpr int NP = DMA ? 1 : (XP > WP ? XP : WP);
+    const uint16_t *xsrc[NP];
+    const uint16_t *wsrc[NP];
+    int xslot[NP], wslot[NP];
+    // Direct path: buffer resources over this tile's rows, so rows past M / N read as zeros, and one
+    // byte offset per operand and lane; pass p adds p * T / CPR rows.
+    __amdgpu_buffer_rsrc_t xr, wr;
+    uint32_t xvoff = 0, wvoff = 0;
+    if constexpr (DMA) {
+        const int row = (wave * 64 + lane) / CPR;
+        const int ch = (lane % CPR) ^ swzc<CPR>(row);
+        const int64_t mrows = min((int64_t)TBM, a.M - m0);
+        xr = make_rsrc((const uint16_t *)a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx * 2));
+        xvoff = (uint32_t)(row * a.ldx + ch * 8) * 2;
+        const bool second = n0 >= a.n0;     // a tile never straddles the w0 / w1 boundary here
+        const int nend = second ? a.N : min(a.N, a.n0);
+        const uint16_t *wbase = second ? (const uint16_t *)a.w1 + (int64_t)(n0 - a.n0) * a.K
+                                       : (const uint16_t *)a.w0 + (int64_t)n0 * a.K;
+        wr = make_rsrc(wbase, (uint32_t)(min(TBN, nend - n0) * a.K * 2));
+        wvoff = (uint32_t)(row * a.K + ch * 8) * 2;
+    } else {
 #pragma unroll
-    for (int p = 0; p < kLoadPasses; ++p) {
-        const int q = tid + p * kGemmThreads, row = q >> 3, ch = q & 7;
-        const int64_t gm = m0 + row;
-        xrow[p] = gm < a.M ? (const uint16_t *)a.x + gm * a.ldx + ch * 8 : nullptr;
-        const int gn = n0 + row;
-        const uint16_t *wp = nullptr;
-        if (gn < a.N) wp = gn < a.n0 ? (const uint16_t *)a.w0 + (int64_t)gn * a.K : (const uint16_t *)a.w1 + (int64_t)(gn - a.n0) * a.K;
-        wrow[p] = wp ? wp + ch * 8 : nullptr;
+        for (int p = 0; p < XP; ++p) {
+            const int slot = tid + p * T;
+            const int row = slot / CPR, chp = slot % CPR;
+            int64_t gm = m0 + row;
+            if (gm >= a.M) gm = a.M - 1;
+            xsrc[p] = (const uint16_t *)a.x + gm * a.ldx + chp * 8;
+            xslot[p] = row * CPR + (chp ^ swzc<CPR>(row));
+        }
+#pragma unroll
+        for (int p = 0; p < WP; ++p) {
+            const int slot = tid + p * T;
+            const int row = slot / CPR, chp = slot % CPR;
+            int gn = n0 + row;
+            if (gn >= a.N) gn = a.N - 1;
+            const uint16_t *wp = gn < a.n0 ? (const uint16_t *)a.w0 + (int64_t)gn * a.K
+                                           : (const uint16_t *)a.w1 + (int64_t)(gn - a.n0) * a.K;
+            wsrc[p] = wp + chp * 8;
+            wslot[p] = row * CPR + (chp ^ swzc<CPR>(row));
+        }
     }
-    uint4 px[kLoadPasses], pw[kLoadPasses];
-    auto gload = [&](int k0) {
+    uint4 px[NP], pw[NP];
+    auto fetch = [&](int kt, auto st) {
+        int ktr = kt + krot;     // rotated k order, see krot
+        if (ktr >= nk) ktr -= nk;
+        const int k0 = kbeg + ktr * TBK;
+        if constexpr (DMA) {
+            const bool in = kt < nk;
 #pragma unroll
-        for (int p = 0; p < kLoadPasses; ++p) {
-            const int q = tid + p * kGemmThreads, ch = q & 7;
-            const bool kin = k0 + ch * 8 < kend;
-            px[p] = (xrow[p] && kin) ? *(const uint4 *)(xrow[p] + k0) : make_uint4(0, 0, 0, 0);
-            pw[p] = (wrow[p] && kin) ? *(const uint4 *)(wrow[p] + k0) : make_uint4(0, 0, 0, 0);
+            for (int p = 0; p < XP; ++p)
+                buffer_copy16_to_lds(xr, in ? xvoff + (uint32_t)(p * (T / CPR) * a.ldx + k0) * 2 : kOutOfRange,
+                                     xs(st) + p * T + wave * 64);
+#pragma unroll
+            for (int p = 0; p < WP; ++p)
+                buffer_copy16_to_lds(wr, in ? wvoff + (uint32_t)(p * (T / CPR) * a.K + k0) * 2 : kOutOfRange,
+                                     ws(st) + p * T + wave * 64);
+        } else {
+#pragma unroll
+            for (int p = 0; p < XP; ++p) {
+                const int ch = (tid + p * T) % CPR;
+                px[p] = (k0 + ch * 8 < kend) ? *(const uint4 *)(xsrc[p] + k0) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int p = 0; p < WP; ++p) {
+                const int ch = (tid + p * T) % CPR;
+                pw[p] = (k0 + ch * 8 < kend) ? *(const uint4 *)(wsrc[p] + k0) : make_uint4(0, 0, 0, 0);
+            }
         }
     };
-    auto lstore = [&](int st) {
+    auto commit = [&](auto st) {   // register-staged path: write the fetched tile to LDS
+        if constexpr (!DMA) {
 #pragma unroll
-        for (int p = 0; p < kLoadPasses; ++p) {
-            const int q = tid + p * kGemmThreads, row = q >> 3, ch = q & 7;
-            sx[st][row * 8 + (ch ^ swz(row))] = px[p];
-            sw[st][row * 8 + (ch ^ swz(row))] = pw[p];
+            for (int p = 0; p < XP; ++p) xs(st)[xslot[p]] = px[p];
+#pragma unroll
+            for (int p = 0; p < WP; ++p) ws(st)[wslot[p]] = pw[p];
         }
     };
-
     f32x16 acc[NB][MB];
 #pragma unroll
     for (int i = 0; i < NB; ++i)
@@ -160,41 +269,77 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs a, int
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    if (nk > 0) {
-        gload(kbeg);
-        lstore(0);
-    }
-    __syncthreads();
-    for (int it = 0; it < nk; ++it) {
-        const int st = it & 1;
-        if (it + 1 < nk) gload(kbeg + (it + 1) * BK);
+    // fragments of one 16-deep k step: NB from the weight tile (A operand), MB from the activation
+    // tile (B operand); two register sets so step ks + 1 is read while step ks multiplies
+    constexpr int KS = TBK / 16;
+    bf16x8 af[2][NB], bfr[2][MB];
+    auto load_frags = [&](auto st, int ks, auto set) {
+        const int ch = ks * 2 + half;
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = ks * 2 + half;
-            bf16x8 af[NB], bfr[MB];
+        for (int i = 0; i < NB; ++i) {
+            const int row = wn * TN + i * 32 + l32;
+            af[set][i] = __builtin_bit_cast(bf16x8, ws(st)[row * CPR + (ch ^ swzc<CPR>(row))]);
+        }
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int row = wn * WN + i * 32 + l32;
-                af[i] = __builtin_bit_cast(bf16x8, sw[st][row * 8 + (ch ^ swz(row))]);
-            }
-#pragma unroll
-            for (int j = 0; j < MB; ++j) {
-                const int row = wm * WM + j * 32 + l32;
-                bfr[j] = __builtin_bit_cast(bf16x8, sx[st][row * 8 + (ch ^ swz(row))]);
-            }
+        for (int j = 0; j < MB; ++j) {
+            const int row = wm * TM + j * 32 + l32;
+            bfr[set][j] = __builtin_bit_cast(bf16x8, xs(st)[row * CPR + (ch ^ swzc<CPR>(row))]);
+        }
+    };
+    auto compute = [&](auto st) {
+        load_frags(st, 0, IC<0>{});
+        static_for<KS>([&](auto ks) {
+            constexpr int cur = ks & 1;
+            // the next step's reads go out before this step's MFMAs, into the other register set
+            if constexpr (ks + 1 < KS) load_frags(st, ks + 1, IC<cur ^ 1>{});
+            sched_fence();
 #pragma unroll
             for (int i = 0; i < NB; ++i)
 #pragma unroll
-                for (int j = 0; j < MB; ++j) acc[i][j] = mfma_32x32x16_bf16(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < MB; ++j) acc[i][j] = mfma_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j]);
+        });
+    };
+
+    if constexpr (DMA) {
+        // Every step copies one tile. Tiles at or past nk are read out of range (zeros, no memory
+        // access), so the loop has no data-dependent branch and a fixed number of copies in flight;
+        // it runs to a multiple of NBUF steps, the extra ones multiplying zeros.
+        static_for<NBUF - 1>([&](auto S) { fetch(S, S); });
+        wait_vmcnt<(NBUF - 2) * kCopies>();                   // tile 0 landed
+        barrier_lds();
+        for (int base = 0; base < nk; base += NBUF) {
+            static_for<NBUF>([&](auto S) {
+                // the stage of tile base + S + NBUF - 1 held the tile consumed before the last barrier
+                fetch(base + S + NBUF - 1, IC<(S + NBUF - 1) % NBUF>{});
+                compute(S);
+                wait_vmcnt<(NBUF - 2) * kCopies>();           // tile base + S + 1 landed
+                barrier_lds();
+            });
         }
-        if (it + 1 < nk) lstore(st ^ 1);
-        __syncthreads();
+        wait_vmcnt<0>();     // no copy may still be writing LDS when the workgroup ends
+    } else {
+        if (nk > 0) {
+            fetch(0, IC<0>{});
+            commit(IC<0>{});
+        }
+        barrier_lds();
+        for (int base = 0; base < nk; base += 2) {
+            static_for<2>([&](auto S) {
+                const int it = base + S;
+                if (it < nk) {
+                    if (it + 1 < nk) fetch(it + 1, IC<1 - S>{});
+                    compute(S);
+                    if (it + 1 < nk) commit(IC<1 - S>{});
+                    barrier_lds();
+                }
+            });
+        }
     }
 
     // ---- epilogue ----
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
-        const int64_t row = m0 + wm * WM + j * 32 + l32;
+        const int64_t row = m0 + wm * TM + j * 32 + l32;
         if (row >= a.M) continue;
         if (PARTIAL) {
             float *pp = a.partial + ((int64_t)sp * a.M + row) * a.N;
@@ -202,7 +347,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs a, int
             for (int i = 0; i < NB; ++i)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const int64_t col = n0 + wn * WN + i * 32 + 8 * jj + 4 * half;
+                    const int64_t col = n0 + wn * TN + i * 32 + 8 * jj + 4 * half;
                     for (int e = 0; e < 4; ++e)
                         if (col + e < a.N) pp[col + e] = acc[i][j][4 * jj + e];
                 }
@@ -213,7 +358,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(GemmArgs a, int
             for (int i = 0; i < NB; ++i)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const int64_t col = n0 + wn * WN + i * 32 + 8 * jj + 4 * half;
+                    const int64_t col = n0 + wn * TN + i * 32 + 8 * jj + 4 * half;
                     if (col < a.N)
                         epilogue4(a, row, zrow, ok, col, acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
                                   acc[i][j][4 * jj + 3]);
@@ -336,8 +481,23 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
         if (a.partial) hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, b, (int32_t)tm, (int32_t)tn, kps);
         else hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, b, (int32_t)tm, (int32_t)tn, kps);
     } else {
-        if (a.partial) hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, b, (int32_t)tm, (int32_t)tn, kps);
-        else hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, b, (int32_t)tm, (int32_t)tn, kps);
+        // direct copies: k tiles whole, 16-byte aligned rows, buffer ranges within 32 bits, and no
+        // tile across the w0 / w1 boundary
+        const bool dma = a.K % BK == 0 && kps % BK == 0 && a.ldx % 8 == 0 && ((uintptr_t)a.x & 15) == 0 &&
+                         ((uintptr_t)a.w0 & 15) == 0 && ((uintptr_t)a.w1 & 15) == 0 &&
+                         (a.n0 >= a.N || a.n0 % BN == 0) && (int64_t)BM * a.ldx * 2 < (1LL << 31) &&
+                         (int64_t)BN * a.K * 2 < (1LL << 31);
+#define IKBO_GEMM(D, P)                                                                                              \
+    hipLaunchKernelGGL((gemm_bf16_t<kWGM, kWGN, kTM, kTN, BK, 2, D, P>), dim3((unsigned)grid), dim3(kGemmThreads), 0, \
+                       s, b, (int32_t)tm, (int32_t)tn, kps)
+        if (dma) {
+            if (a.partial) IKBO_GEMM(true, true);
+            else IKBO_GEMM(true, false);
+        } else {
+            if (a.partial) IKBO_GEMM(false, true);
+            else IKBO_GEMM(false, false);
+        }
+#undef IKBO_GEMM
     }
     return hipGetLastError();
 }

@@ -60,7 +60,10 @@ def test_tiny_fp32_workload():
 
 
 @pytest.mark.parametrize("act", ["gelu", "none"])
-@pytest.mark.parametrize("shape", [(136, 264, 72, 200), (64, 8, 40, 203), (4096, 512, 256, 256)])
+# (k_req, k_cand, n_req, n_cand): k tails, tiny K, long split-K request GEMM, and with K a
+# multiple of 64 (direct LDS copies) ragged N over several column tiles
+@pytest.mark.parametrize("shape", [(136, 264, 72, 200), (64, 8, 40, 203), (4096, 512, 256, 256),
+                                   (128, 192, 256, 200), (64, 256, 520, 1000)])
 def test_bf16_ragged_shapes(act, shape):
     k_req, k_cand, n_req, n_cand = shape
     counts = np.array([1, 300, 0, 77, 513, 2, 40])
