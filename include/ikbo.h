@@ -83,6 +83,9 @@ const char *ikbo_last_error_message(void);
  *       given they define the grouping and cand_to_req is not read.
  * num_heads      H >= 1 (queries and keys share the head count)
  * head_dim       bf16: 64 or 128; fp32: a multiple of 4 in [4, 128]
+ *       bf16 also needs each request's K (and V) rows to span fewer than 2^31 bytes,
+ *       L_r * num_heads * head_dim * 2 < 2^31: a larger kv_len is rejected (IKBO_UNSUPPORTED);
+ *       with kv_cu_seqlens and kv_len = 0 a longer request yields NaN output rows.
  * softmax_scale  <= 0 selects 1/sqrt(head_dim)
  * out   [num_cand, q_len, num_heads, head_dim] (out_dtype). Rows of a request with L_r = 0 and
  *       rows of candidates with no valid request are written as zeros.

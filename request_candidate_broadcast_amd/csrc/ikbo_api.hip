@@ -224,6 +224,8 @@ int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len, const void 
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(IKBO_UNSUPPORTED, "dtype in %d out %d", in_dtype, out_dtype);
     if (in_dtype == IKBO_BF16 && head_dim != 64 && head_dim != 128)
         return fail(IKBO_UNSUPPORTED, "bf16 DCA is built for head_dim 64 and 128, got %d", head_dim);
+    if (in_dtype == IKBO_BF16 && (int64_t)kv_len * num_heads * head_dim * 2 >= (1LL << 31))
+        return fail(IKBO_UNSUPPORTED, "bf16 DCA needs L_r * num_heads * head_dim * 2 < 2^31 bytes (kv_len %d)", kv_len);
     if (in_dtype == IKBO_F32 && (head_dim % 4 || head_dim > 128))
         return fail(IKBO_UNSUPPORTED, "fp32 DCA needs head_dim a multiple of 4 up to 128, got %d", head_dim);
     int rc = check_index_args(cand_to_req, req_cand_offsets, index_flags, C);

@@ -14,17 +14,16 @@
 //    tiles run together on one XCD and share its L2 (the MI355X form of the grid reorder of
 //    Sec. 4.3.1).
 //  - bf16 path: 8 waves x 32 query rows. The K/V tile of BLOCK_N keys is staged once in LDS
-//    (double-buffered) and read by all 8 waves. Scores are computed transposed, S^T = K Q^T, with
+//    and read by all 8 waves. Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16 so each lane owns one query column: the softmax max is a per-lane
 //    reduction plus one exchange between the two 32-lane halves, and the per-lane partial sums are
-//    combined once at the end. The accumulator of S^T is reused in registers as the B operand of
-//    O^T += V^T P^T; V^T comes from LDS through ds_read_b64_tr_b16, which transposes 16-bit data
-//    across each 16-lane group.
-//  - Online softmax in the exp2 domain with the softmax scale folded into one FMA, and lazy
-//    rescaling: a query's reference max is only raised when the tile max exceeds it by more than
-//    kTau (log2 units), so most tiles skip the O rescale; the final O / l is exact in real
-//    arithmetic for any reference value. The decision is per query, so a row's result does not
-//    depend on which other rows share its tile.
+//    combined once at the end. The bf16 weights P^T are the B operand of O^T += V^T P^T; V^T comes
+//    from LDS through ds_read_b64_tr_b16, which transposes 16-bit data across each 16-lane group.
+//  - Softmax in the exp2 domain with the softmax scale folded into one FMA, against a fixed
+//    per-query reference (the max of the first tile), so O is never rescaled; O / l is exact in
+//    real arithmetic for any reference. A query whose sums leave the fp32 range is redone with its
+//    exact max (a rare second and third pass over its keys); the decision is per query, so a
+//    row's result does not depend on which other rows share its tile.
 #include "ikbo_device.h"
 #include "ikbo_launch.h"
 
@@ -48,13 +47,6 @@ __device__ __forceinline__ int64_t find_request(const int32_t *tile_start, int64
     }
     return lo;
 }
-
-// LDS swizzles (16-byte chunk index XOR a function of the key row) so that the MFMA operand
-// reads of K (ds_read_b128, 32 consecutive keys at one chunk) and the transposed reads of V
-// (ds_read_b64_tr_b16, 4 consecutive keys x 2 chunks per 16 lanes) hit distinct banks.
-template <int D>
-__device__ __forceinline__ int swz_k(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
-__device__ __forceinline__ int swz_v(int key) { return (key & 3) << 1; }
 
 struct TileInfo {
     int64_t r, h, qb, rows, cand0, kv_row0, Lr;
@@ -99,18 +91,22 @@ __device__ __forceinline__ void row_source(const DcaArgs &a, const TileInfo &ti,
 // ----------------------------------------------------------------------------------------------
 // bf16 inputs, D in {64, 128}, MFMA path.
 //
-// Template parameters: NW waves per workgroup, NG groups of 32 query columns per wave, NKB
-// 32-key blocks per K/V tile, NBUF LDS stages, LATE = copy the next tiles in after this tile's
-// V fragments are read (else at the top of the tile). With NG = 2 the work of one tile is
-// ordered so the softmax VALU work of one group overlaps the MFMA work of the other
-// (scheduling fences keep the phases apart):
-//   A: S0 = K Q0^T                     (MFMA)
-//   B: S1 = K Q1^T        | softmax(S0) (MFMA | VALU)
-//   C: O0 += V^T P0^T     | softmax(S1)
-//   D: O1 += V^T P1^T
-// K fragments are read from LDS once per tile and used by every group, likewise the V^T
-// fragments. K/V tiles are copied global -> LDS directly (no register staging); one barrier per
-// tile.
+// Template parameters: NW waves per workgroup, each owning 32 query rows (one column of S^T per
+// lane); NKB 32-key blocks per K/V tile; NBUF LDS stages; KPD / VPD how many k16 steps of K
+// fragments / 32-dim blocks of V^T fragments are read ahead of the MFMAs that use them. Eight
+// waves put two on every SIMD, so the softmax VALU work of one overlaps the MFMAs of the other in
+// hardware; streaming the fragments from LDS step by step (instead of holding a whole tile) keeps
+// a wave within the 256 registers that two waves per SIMD leave it. One barrier per tile.
+//
+// LDS layout: K rows are padded to D*2 + 16 bytes, so 16 consecutive keys read at one 16-byte
+// column fall in 16 distinct bank groups without a swizzle, and every K operand read is one
+// per-lane base plus a compile-time offset. V rows are padded to D*2 + 64 bytes, so the transposed
+// reads (4 keys x 64 bytes per 32 lanes) hit distinct banks, again base plus constant. Tiles are
+// copied with buffer loads straight into LDS: each wave instruction fills 64 consecutive 16-byte
+// slots, so a lane's source is the (key, column) of its slot. Pad slots, and keys at or past L_r
+// (the buffer range covers the request's rows only), read as zeros without touching memory.
+// Each stage is its own LDS variable and stage indices are compile-time constants (the tile loop
+// is unrolled by NBUF), so reads of one stage are not held back by copies into another.
 
 // Cross-half combine: v_permlane32_swap exchanges the two 32-lane halves, so the max (or sum) of
 // both results is the value over lanes l and l ^ 32.
@@ -144,304 +140,295 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[NKB]) {
     return half_swap_max(mx);
 }
 
-// p = 2^(s * scale * log2(e) - m_ref) against a fixed per-query reference; accumulates the row
-// sum and packs the bf16 B operands of the PV MFMAs.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// p = 2^(s * scale * log2(e) - m_ref) against a fixed per-query reference; packs the bf16 B
+// operands of the PV MFMAs and adds the packed (rounded) weights to the row sum, so the sum
+// normalises exactly the weights the PV MFMAs use.
 template <int NKB>
 __device__ __forceinline__ void exp_tile(f32x16 (&s)[NKB], bf16x8 (&pb)[NKB][2], float &l, float cl2, float mneg) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j], cl2, mneg));
-            s[kb][j] = p;
-            l += p;
-        }
+        for (int j = 0; j < 16; ++j) s[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j], cl2, mneg));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) pb[kb][u][e] = (__bf16)s[kb][8 * u + e];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const bf16x2 pr = {pb[kb][u][e], pb[kb][u][e + 1]};
+                l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+            }
+        }
 }
 
-template <int D, int NW, int NG, int NKB, int NBUF, bool LATE>
+template <int D, int NW, int NKB, int NBUF, int KPD, int VPD>
 __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
     constexpr int BN = NKB * 32;                       // keys per tile
-    constexpr int BM = NW * NG * 32;                   // stacked query rows per workgroup
+    constexpr int BM = NW * 32;                        // stacked query rows per workgroup
     constexpr int CPR = D / 8;                         // 16-byte chunks per key row
-    constexpr int kTileChunks = BN * CPR;              // chunks per K (or V) tile
-    constexpr int kThreads = NW * 64;
-    constexpr int kLoadPasses = kTileChunks / kThreads;
-    static_assert(kTileChunks % kThreads == 0, "tile load must split evenly");
-    constexpr int kCopiesPerTile = 2 * kLoadPasses;    // global -> LDS instructions per tile (K and V)
-    static_assert(NBUF == 2 || (NBUF == 3 && LATE), "three stages are filled late");
-    constexpr int KS = D / 16;                         // k16 steps over the head dim
-    constexpr int DB = D / 32;                         // 32-row blocks of O^T
+    constexpr int KSR = CPR + 1, VSR = CPR + 4;        // 16-byte slots per padded K / V row
+    constexpr int VROW = VSR * 16;                     // bytes per padded V row
+    constexpr int kInstrK = ((BN * KSR + 63) / 64 + NW - 1) / NW * NW;
+    constexpr int kInstrV = ((BN * VSR + 63) / 64 + NW - 1) / NW * NW;
+    constexpr int kPassK = kInstrK / NW, kPassV = kInstrV / NW;
+    constexpr int kCopiesPerTile = kPassK + kPassV;
+    static_assert(NBUF == 2 || NBUF == 3, "two or three LDS stages");
+    static_assert((NBUF - 2) * kCopiesPerTile < 64, "vmcnt range");
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr uint32_t kOutOfRange = 0x80000000u;
 
-    __shared__ uint4 smem[NBUF][2][kTileChunks];       // [stage][K=0 / V=1][chunk]
+    __shared__ uint4 k_s0[kInstrK * 64], k_s1[kInstrK * 64], k_s2[NBUF > 2 ? kInstrK * 64 : 1];
+    __shared__ uint4 v_s0[kInstrV * 64], v_s1[kInstrV * 64], v_s2[NBUF > 2 ? kInstrV * 64 : 1];
+    auto k_lds = [&](auto S) __attribute__((always_inline)) -> uint4 * {
+        if constexpr (decltype(S)::value == 0) return k_s0;
+        else if constexpr (decltype(S)::value == 1) return k_s1;
+        else return k_s2;
+    };
+    auto v_lds = [&](auto S) __attribute__((always_inline)) -> uint4 * {
+        if constexpr (decltype(S)::value == 0) return v_s0;
+        else if constexpr (decltype(S)::value == 1) return v_s1;
+        else return v_s2;
+    };
 
     TileInfo ti;
     if (!decode_tile(a, BM, ti)) return;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, half = lane >> 5;
     const int64_t HD = (int64_t)a.H * D;
 
-    // ---- the lane's query rows (one column of S^T per group) ----
-    bool rvalid[NG];
-    int64_t cand[NG];
-    int tok[NG];
-    bf16x8 qf[NG][KS];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int64_t srow = ti.qb * BM + wave * (NG * 32) + g * 32 + l32;
-        rvalid[g] = srow < ti.rows;
-        cand[g] = 0;
-        tok[g] = 0;
-        if (rvalid[g]) row_source(a, ti, srow, cand[g], tok[g]);
-        const uint16_t *qp = (const uint16_t *)a.q + ((cand[g] * a.Lq + tok[g]) * HD + ti.h * D) + half * 8;
+    // ---- the lane's query row (one column of S^T) ----
+    const int64_t srow = ti.qb * BM + wave * 32 + l32;
+    const bool rvalid = srow < ti.rows;
+    int64_t cand = 0;
+    int tok = 0;
+    if (rvalid) row_source(a, ti, srow, cand, tok);
+    bf16x8 qf[KS];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + ((cand * a.Lq + tok) * HD + ti.h * D) + half * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 u = rvalid[g] ? *(const uint4 *)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-            qf[g][ks] = __builtin_bit_cast(bf16x8, u);
+            uint4 u = rvalid ? *(const uint4 *)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+            qf[ks] = __builtin_bit_cast(bf16x8, u);
         }
     }
 
-    // ---- K/V tile copies: global -> LDS direct ----
-    // Each wave instruction fills 64 consecutive 16-byte LDS slots; the lane that fills slot
-    // (key, c') reads chunk c' ^ swizzle(key) of that key row, which realises the swizzled layout.
-    // Rows past L_r are read from row L_r - 1 instead: their scores are masked to -inf, so they
-    // get weight exactly 0 and their finite values do not matter.
-    const uint16_t *kbase = (const uint16_t *)a.k + ti.kv_row0 * HD + ti.h * D;
-    const uint16_t *vbase = (const uint16_t *)a.v + ti.kv_row0 * HD + ti.h * D;
-    const int Lr = (int)ti.Lr;
-    auto dma = [&](int n0, int st) {
+    // ---- K/V tile copies: buffer -> LDS ----
+    const uint16_t *kbase = uniform_ptr((const uint16_t *)a.k + ti.kv_row0 * HD + ti.h * D);
+    const uint16_t *vbase = uniform_ptr((const uint16_t *)a.v + ti.kv_row0 * HD + ti.h * D);
+    const int Lr = __builtin_amdgcn_readfirstlane((int)ti.Lr);
+    uint32_t koff[kPassK], voff[kPassV];
 #pragma unroll
-        for (int p = 0; p < kLoadPasses; ++p) {
-            const int slot0 = p * kThreads + wave * 64;
-            const int slot = slot0 + lane, key = slot / CPR, chp = slot % CPR;
-            const int row = min(n0 + key, Lr - 1);
-            const int64_t roff = (int64_t)row * HD;
-            copy16_to_lds(kbase + roff + (chp ^ swz_k<D>(key)) * 8, &smem[st][0][slot0]);
-            copy16_to_lds(vbase + roff + (chp ^ swz_v(key)) * 8, &smem[st][1][slot0]);
-        }
+    for (int p = 0; p < kPassK; ++p) {
+        const int slot = (p * NW + wave) * 64 + lane, key = slot / KSR, c = slot % KSR;
+        koff[p] = key < BN && c < CPR ? (uint32_t)(key * HD + c * 8) * 2 : kOutOfRange;
+    }
+#pragma unroll
+    for (int p = 0; p < kPassV; ++p) {
+        const int slot = (p * NW + wave) * 64 + lane, key = slot / VSR, c = slot % VSR;
+        voff[p] = key < BN && c < CPR ? (uint32_t)(key * HD + c * 8) * 2 : kOutOfRange;
+    }
+    // Buffer resources over the request's K / V rows (keys at or past L_r read as zeros); the
+    // tile's first row goes into the lane offsets. The host keeps L_r * H * D * 2 below 2^31.
+    const uint32_t req_bytes = (uint32_t)((int64_t)Lr * HD * 2);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, req_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, req_bytes);
+    auto dma = [&](int n0, auto S) __attribute__((always_inline)) {
+        const uint32_t toff = (uint32_t)min((int64_t)n0 * HD * 2, (int64_t)0x7fff0000);
+#pragma unroll
+        for (int p = 0; p < kPassK; ++p) buffer_copy16_to_lds(kr, koff[p] + toff, k_lds(S) + (p * NW + wave) * 64);
+#pragma unroll
+        for (int p = 0; p < kPassV; ++p) buffer_copy16_to_lds(vr, voff[p] + toff, v_lds(S) + (p * NW + wave) * 64);
     };
 
     const float cl2 = a.scale * 1.4426950408889634f;
-
-    // lane constants of the transposed V read
     const int g16 = lane >> 4, s16 = lane & 15;
     const int tr_dsub = (g16 & 1) * 16 + 4 * (s16 & 3);
     const int tr_key = 4 * (g16 >> 1) + (s16 >> 2);
+    const int k_lane = l32 * KSR + half;
+    const int v_lane = tr_key * VROW + tr_dsub * 2;
 
-    // K fragments of one tile (A operands of S^T = K Q^T)
-    auto k_frags = [&](int st, bf16x8 (&kf)[KS][NKB]) {
-        const uint4 *ks_lds = smem[st][0];
+    // a request whose K/V block does not fit the 31-bit buffer range gets NaN rows (the host
+    // rejects such calls when it knows a bound on L_r)
+    const bool fits = (int64_t)Lr * HD * 2 < (1LL << 31);
+    const int ntiles = fits ? (Lr + BN - 1) / BN : 0;
+    const bool ragged = (Lr % BN) != 0;
+
+    f32x16 o[DB];
+    float l = 0.0f, mref = 0.0f, mx = -INFINITY;
+    auto clear = [&]() __attribute__((always_inline)) {
+        l = 0.0f;
+        mx = -INFINITY;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const int key = kb * 32 + l32, ch = ks * 2 + half;
-                kf[ks][kb] = __builtin_bit_cast(bf16x8, ks_lds[key * CPR + (ch ^ swz_k<D>(key))]);
-            }
+            for (int j = 0; j < 16; ++j) o[db][j] = 0.0f;
     };
-    auto s_tile = [&](const bf16x8 (&kf)[KS][NKB], const bf16x8 (&q)[KS], f32x16 (&s)[NKB]) {
+    clear();
+
+    bf16x8 pb[NKB][2];      // bf16 weights of the last scored tile (B operands of the PV MFMAs)
+
+    // Scores of tile `it` in stage S and their softmax weights into pb (MAXONLY: the per-query
+    // max only). MASK: the ragged last tile. INIT: the first tile sets m_ref.
+    auto score = [&](int it, auto S, auto mask, auto init, auto maxonly) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask)::value;
+        constexpr bool INIT = decltype(init)::value;
+        constexpr bool MAXONLY = decltype(maxonly)::value;
+        // S^T = K Q^T, K fragments streamed per k16 step
+        f32x16 sc[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s[kb][j] = 0.0f;
+            for (int j = 0; j < 16; ++j) sc[kb][j] = 0.0f;
+        const uint4 *kp = k_lds(S) + k_lane;
+        bf16x8 kf[KPD + 1][NKB];     // KPD steps of reads in flight ahead of the MFMAs
+        static_for<KPD>([&](auto ks) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int kb = 0; kb < NKB; ++kb) kf[ks][kb] = __builtin_bit_cast(bf16x8, kp[kb * 32 * KSR + ks * 2]);
+        });
+        static_for<KS>([&](auto ks) {
+            constexpr int cur = ks % (KPD + 1);
+            if constexpr (ks + KPD < KS) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma_32x32x16_bf16(kf[ks][kb], q[ks], s[kb]);
+                for (int kb = 0; kb < NKB; ++kb)
+                    kf[(ks + KPD) % (KPD + 1)][kb] = __builtin_bit_cast(bf16x8, kp[kb * 32 * KSR + (ks + KPD) * 2]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) sc[kb] = mfma_32x32x16_bf16(kf[cur][kb], qf[ks], sc[kb]);
+            sched_fence();     // keeps the reads KPD steps ahead, not hoisted further (registers)
+        });
+        if (MASK) mask_tile<NKB>(sc, Lr - it * BN, half);
+        if constexpr (MAXONLY) {
+            mx = fmaxf(mx, tile_max<NKB>(sc));
+        } else {
+            if (INIT && it == 0) mref = tile_max<NKB>(sc) * cl2;
+            exp_tile<NKB>(sc, pb, l, cl2, -mref);
+        }
     };
-    // V^T fragments of one tile (A operands of O^T += V^T P^T) through the transposing LDS read
-    auto v_frags = [&](int st, bf16x8 (&vf)[DB][NKB][2]) {
-        const char *vs_lds = (const char *)smem[st][1];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int dcol = db * 32 + tr_dsub;
-            const int chunk = dcol >> 3, sub = (dcol & 7) * 2;
+    // O^T += V^T P^T for the tile in stage S with the weights in pb, V^T streamed per 32 dims
+    auto pv = [&](auto S) __attribute__((always_inline)) {
+        const char *vp = (const char *)v_lds(S) + v_lane;
+        bf16x8 vf[VPD + 1][NKB][2];
+        auto vload = [&](int db, int set) __attribute__((always_inline)) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const int key0 = kb * 32 + 16 * u + tr_key;
-                    const int key1 = key0 + 8;
-                    i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(vs_lds + (key0 * CPR + (chunk ^ swz_v(key0))) * 16 + sub));
-                    i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(vs_lds + (key1 * CPR + (chunk ^ swz_v(key1))) * 16 + sub));
-                    typedef short i16x8 __attribute__((ext_vector_type(8)));
-                    vf[db][kb][u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    const int o0 = (kb * 32 + 16 * u) * VROW + db * 64;
+                    i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + o0));
+                    i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + o0 + 8 * VROW));
+                    vf[set][kb][u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
-        }
-    };
-    auto pv_tile = [&](const bf16x8 (&vf)[DB][NKB][2], const bf16x8 (&pb)[NKB][2], f32x16 (&o)[DB]) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
+        };
+        static_for<VPD>([&](auto db) { vload(db, db); });
+        static_for<DB>([&](auto db) {
+            constexpr int cur = db % (VPD + 1);
+            if constexpr (db + VPD < DB) vload(db + VPD, (db + VPD) % (VPD + 1));
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) o[db] = mfma_32x32x16_bf16(vf[db][kb][u], pb[kb][u], o[db]);
-    };
-
-    const int ntiles = (Lr + BN - 1) / BN;
-    const bool ragged = (Lr % BN) != 0;
-
-    // ---- one pass over the keys ----
-    // Softmax weights are taken against a fixed per-query reference m_ref (no running rescale of
-    // O): O' = sum_j 2^(s_j c - m_ref) v_j and l' = sum_j 2^(s_j c - m_ref) give O = O' / l' exactly
-    // in real arithmetic for any m_ref. With INIT the reference is the max of the first tile;
-    // later tiles may exceed it, and a query whose sums overflow is redone with its true max.
-    // With MAXONLY the pass only computes scores and leaves each query's exact max in m_ref.
-    f32x16 o[NG][DB];
-    float l[NG], mref[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        l[g] = 0.0f;
-        mref[g] = 0.0f;
-    }
-    auto pass = [&](auto init, auto maxonly) {
-        constexpr bool INIT = decltype(init)::value;
-        constexpr bool MAXONLY = decltype(maxonly)::value;
-        float mx[NG];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            l[g] = 0.0f;
-            mx[g] = -INFINITY;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) o[g][db][j] = 0.0f;
-        }
-        // prologue: the first tile (and with three stages the second) in flight, the first landed
-        if (ntiles > 0) dma(0, 0);
-        if (NBUF == 3 && ntiles > 1) {
-            dma(BN, 1);
-            wait_vmcnt<kCopiesPerTile>();
-        } else {
-            wait_all();
-        }
-        __syncthreads();
-        auto tile = [&](int it, auto first, auto masked) {
-            constexpr bool FIRST = decltype(first)::value;
-            constexpr bool MASK = decltype(masked)::value;
-            const int st = it % NBUF;
-            const int n0 = it * BN;
-            const int ahead = it + NBUF - 1;               // the tile copied in during this one
-            const bool copy = ahead < ntiles;
-            if (!LATE && copy) dma(ahead * BN, ahead % NBUF);
-            f32x16 s[NG][NKB];
-            bf16x8 p[NG][NKB][2];
-            bf16x8 kf[KS][NKB];
-            bf16x8 vf[DB][NKB][2];
-            k_frags(st, kf);
-            auto softmax = [&](int g) {
-                if (MASK) mask_tile<NKB>(s[g], Lr - n0, half);
-                if (MAXONLY) {
-                    mx[g] = fmaxf(mx[g], tile_max<NKB>(s[g]));
-                } else {
-                    if (INIT && FIRST) mref[g] = tile_max<NKB>(s[g]) * cl2;
-                    exp_tile<NKB>(s[g], p[g], l[g], cl2, -mref[g]);
-                }
-            };
-            s_tile(kf, qf[0], s[0]);                                         // A
+                for (int u = 0; u < 2; ++u) o[db] = mfma_32x32x16_bf16(vf[cur][kb][u], pb[kb][u], o[db]);
             sched_fence();
-            if (NG == 2) {
-                s_tile(kf, qf[NG - 1], s[NG - 1]);                           // B
-                softmax(0);
-                sched_fence();
-            } else {
-                softmax(0);
-            }
-            if (!MAXONLY) v_frags(st, vf);
-            if (LATE && copy) dma(ahead * BN, ahead % NBUF);
-            if (!MAXONLY) {
-                pv_tile(vf, p[0], o[0]);                                     // C
-                if (NG == 2) {
-                    softmax(NG - 1);
-                    sched_fence();
-                    pv_tile(vf, p[NG - 1], o[NG - 1]);                       // D
-                }
-            } else if (NG == 2) {
-                softmax(NG - 1);
-            }
-            // the next tile must have landed; with three stages the one after may stay in flight
-            if (NBUF == 3 && it + 2 < ntiles) wait_vmcnt<kCopiesPerTile>();
-            else wait_vmcnt<0>();
-            __syncthreads();
-        };
-        const std::true_type T;
-        const std::false_type F;
-        if (ntiles == 1) {
-            if (ragged) tile(0, T, T); else tile(0, T, F);
-        } else if (ntiles > 1) {
-            tile(0, T, F);
-            for (int it = 1; it + 1 < ntiles; ++it) tile(it, F, F);
-            if (ragged) tile(ntiles - 1, F, T); else tile(ntiles - 1, F, F);
-        }
-        if (MAXONLY) {
-#pragma unroll
-            for (int g = 0; g < NG; ++g) mref[g] = mx[g] * cl2;
-        }
+        });
     };
+    // One whole tile, nothing else in flight (the overflow redo)
+    auto tile = [&](int it, auto S, auto mask, auto maxonly) __attribute__((always_inline)) {
+        score(it, S, mask, std::false_type(), maxonly);
+        if constexpr (!decltype(maxonly)::value) pv(S);
+        wait_vmcnt<0>();
+        barrier_lds();
+    };
+    const std::true_type T;
+    const std::false_type F;
 
-    pass(std::true_type(), std::false_type());
-
-    // ---- overflow check: redo the tile for the queries whose sums left the fp32 range ----
-    bool bad[NG];
-    bool any_bad = false;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        bool b = !(half_swap_sum(l[g]) < INFINITY);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) b |= !(fabsf(o[g][db][j]) < INFINITY);
-        // a query column lives in lanes l and l ^ 32: both halves must take the same decision
-        bad[g] = half_swap_max(b ? 1.0f : 0.0f) > 0.0f && rvalid[g];
-        any_bad |= bad[g];
+    // ---- main pass: copies run NBUF - 1 tiles ahead; the ragged last tile is masked ----
+    auto step = [&](int it, auto S, auto mask) __attribute__((always_inline)) {
+        // the stage of tile it + NBUF - 1 held tile it - 1, finished before the last barrier
+        dma((it + NBUF - 1) * BN, IC<(S + NBUF - 1) % NBUF>{});
+        score(it, S, mask, T, F);
+        pv(S);
+        wait_vmcnt<(NBUF - 2) * kCopiesPerTile>();     // tile it + 1 landed
+        barrier_lds();
+    };
+    if (ntiles > 0) {
+        static_for<NBUF - 1>([&](auto S) { dma(S * BN, S); });
+        wait_vmcnt<(NBUF - 2) * kCopiesPerTile>();
+        barrier_lds();
+        const int nfull = ragged ? ntiles - 1 : ntiles;
+        for (int it0 = 0; it0 < nfull; it0 += NBUF)
+            static_for<NBUF>([&](auto J) {
+                if (it0 + J < nfull) step(it0 + J, J, F);
+            });
+        if (ragged) {
+            const int st = (ntiles - 1) % NBUF;
+            static_for<NBUF>([&](auto S) {
+                if (st == S) step(ntiles - 1, S, T);
+            });
+        }
+        wait_vmcnt<0>();     // copies past the end (zeros) land before the stages are reused
+        barrier_lds();
     }
-    if (__syncthreads_or(any_bad)) {
-        float keep[NG];
+
+    // ---- overflow check and redo, one tile copied at a time ----
+    bool b = !(half_swap_sum(l) < INFINITY);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) keep[g] = mref[g];
-        pass(std::false_type(), std::true_type());               // exact max per query
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) mref[g] = bad[g] ? mref[g] : keep[g];
-        pass(std::false_type(), std::false_type());              // redo; unchanged queries repeat bit for bit
+        for (int j = 0; j < 16; ++j) b |= !(fabsf(o[db][j]) < INFINITY);
+    const bool bad = half_swap_max(b ? 1.0f : 0.0f) > 0.0f && rvalid;
+    if (__syncthreads_or(bad)) {
+        const float keep = mref;
+        clear();
+        for (int it = 0; it < ntiles; ++it) {
+            dma(it * BN, IC<0>{});
+            wait_vmcnt<0>();
+            barrier_lds();
+            if (ragged && it == ntiles - 1) tile(it, IC<0>{}, T, T);
+            else tile(it, IC<0>{}, F, T);
+        }
+        mref = bad ? mx * cl2 : keep;
+        clear();
+        for (int it = 0; it < ntiles; ++it) {
+            dma(it * BN, IC<0>{});
+            wait_vmcnt<0>();
+            barrier_lds();
+            if (ragged && it == ntiles - 1) tile(it, IC<0>{}, T, F);
+            else tile(it, IC<0>{}, F, F);
+        }
     }
 
-    // ---- epilogue: O = O^T / l, store rows ----
+    // ---- epilogue: O = O^T / l ----
+    const float l_tot = half_swap_sum(l);
+    if (!rvalid) return;
+    const float inv = !fits ? __builtin_nanf("") : l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const int64_t obase = (cand * a.Lq + tok) * HD + ti.h * D;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const float l_tot = half_swap_sum(l[g]);
-        if (!rvalid[g]) continue;
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        const int64_t obase = (cand[g] * a.Lq + tok[g]) * HD + ti.h * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int d = db * 32 + 8 * jj + 4 * half;
-                const float v0 = o[g][db][4 * jj + 0] * inv, v1 = o[g][db][4 * jj + 1] * inv;
-                const float v2 = o[g][db][4 * jj + 2] * inv, v3 = o[g][db][4 * jj + 3] * inv;
-                if (a.out_f32) {
-                    *(float4 *)((float *)a.out + obase + d) = make_float4(v0, v1, v2, v3);
-                } else {
-                    *(uint2 *)((uint16_t *)a.out + obase + d) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-                }
+        for (int jj = 0; jj < 4; ++jj) {
+            const int d = db * 32 + 8 * jj + 4 * half;
+            const float v0 = o[db][4 * jj + 0] * inv, v1 = o[db][4 * jj + 1] * inv;
+            const float v2 = o[db][4 * jj + 2] * inv, v3 = o[db][4 * jj + 3] * inv;
+            if (a.out_f32) {
+                *(float4 *)((float *)a.out + obase + d) = make_float4(v0, v1, v2, v3);
+            } else {
+                *(uint2 *)((uint16_t *)a.out + obase + d) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
             }
-    }
+        }
 }
 
 // The configuration the library launches, per head dim.
 template <int D>
 struct DcaBf16Config {
-    static constexpr int NW = 4, NG = 2, NKB = 2, NBUF = 3;
-    static constexpr bool LATE = true;
-    static constexpr int BM = NW * NG * 32;
+    // 8 waves x 32 query rows, 64-key tiles, two LDS stages, K reads two k16 steps ahead
+    static constexpr int NW = 8, NKB = 2, NBUF = 2, KPD = 2, VPD = 1;
+    static constexpr int BM = NW * 32;
 };
 
 // ----------------------------------------------------------------------------------------------
@@ -546,11 +533,11 @@ hipError_t launch_dca(const DcaArgs &a, hipStream_t s) {
         hipLaunchKernelGGL(dca_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
     } else if (a.D == 128) {
         using C = DcaBf16Config<128>;
-        hipLaunchKernelGGL((dca_bf16_kernel<128, C::NW, C::NG, C::NKB, C::NBUF, C::LATE>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((dca_bf16_kernel<128, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD>), dim3((unsigned)grid),
                            dim3(C::NW * 64), 0, s, a);
     } else if (a.D == 64) {
         using C = DcaBf16Config<64>;
-        hipLaunchKernelGGL((dca_bf16_kernel<64, C::NW, C::NG, C::NKB, C::NBUF, C::LATE>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((dca_bf16_kernel<64, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD>), dim3((unsigned)grid),
                            dim3(C::NW * 64), 0, s, a);
     } else {
         return hipErrorInvalidValue;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace ikbo {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -36,6 +38,18 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Compile-time loop: f(IC<0>), f(IC<1>), ..., f(IC<N-1>).
+template <int I>
+using IC = std::integral_constant<int, I>;
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(IC<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Thin wrappers of target builtins, so generic lambdas inside kernels only call device functions.
 // No instruction is moved across a scheduling fence.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -60,6 +74,15 @@ __device__ __forceinline__ void barrier_lds() {
 // LDS slots starting at lds_wave_base (taken from the first lane), lane i slot i.
 __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_wave_base) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
+// A pointer that is the same in every lane, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t u = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (T *)(((uint64_t)hi << 32) | lo);
 }
 
 // Raw buffer resource over [base, base + bytes): loads at offsets past the end return zero. The

@@ -16,8 +16,6 @@
 // The request GEMM ([Y_r | Z] = x_r [W_RR; W_CR]^T, a small M = num_req) runs split-K into fp32
 // partial sums, reduced in a fixed order by a second kernel that also applies the request-group
 // epilogue; results are deterministic.
-#include <utility>
-
 #include "ikbo_device.h"
 #include "ikbo_launch.h"
 
@@ -115,18 +113,6 @@ __device__ __forceinline__ bool row_request(const GemmArgs &a, int64_t row, int6
 template <int CPR>
 __device__ __forceinline__ int swzc(int row) { return CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
 
-template <int I>
-using IC = std::integral_constant<int, I>;
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-    (f(IC<I>{}), ...);
-}
-// f(IC<0>), f(IC<1>), ..., f(IC<N-1>)
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL>
 __global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t tiles_m, int32_t tiles_n,
                                                             int32_t k_per_split) {
@@ -177,7 +163,8 @@ __global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t
     // tile and the others find it there, instead of all of them waiting on the same miss.
     const int krot = nk > 0 ? (nt & 3) % nk : 0;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // uniform: LDS copy bases in SGPRs
     const int l32 = lane & 31, half = lane >> 5;
     const int wn = wave / WGM, wm = wave % WGM;
 
