@@ -166,17 +166,18 @@ __device__ __forceinline__ void exp_tile(f32x16 (&s)[NKB], bf16x8 (&pb)[NKB][2],
         }
 }
 
-template <int D, int NW, int NKB, int NBUF, int KPD, int VPD>
+template <int D, int NW, int NKB, int NBUF, int KPD, int VPD, int COPYAT>
 __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
     constexpr int BN = NKB * 32;                       // keys per tile
     constexpr int BM = NW * 32;                        // stacked query rows per workgroup
     constexpr int CPR = D / 8;                         // 16-byte chunks per key row
     constexpr int KSR = CPR + 1, VSR = CPR + 4;        // 16-byte slots per padded K / V row
     constexpr int VROW = VSR * 16;                     // bytes per padded V row
-    constexpr int kInstrK = ((BN * KSR + 63) / 64 + NW - 1) / NW * NW;
-    constexpr int kInstrV = ((BN * VSR + 63) / 64 + NW - 1) / NW * NW;
-    constexpr int kPassK = kInstrK / NW, kPassV = kInstrV / NW;
-    constexpr int kCopiesPerTile = kPassK + kPassV;
+    // wave instructions per K / V tile (64 slots each); wave w issues instructions w, w + NW, ...
+    constexpr int kInstrK = (BN * KSR + 63) / 64, kInstrV = (BN * VSR + 63) / 64;
+    constexpr int kPassK = (kInstrK + NW - 1) / NW, kPassV = (kInstrV + NW - 1) / NW;
+    constexpr int kCopiesPerTile = kPassK + kPassV;     // at most, per wave
+    static_assert(NBUF == 2, "copies of the next tile are waited for in full at each barrier");
     static_assert(NBUF == 2 || NBUF == 3, "two or three LDS stages");
     static_assert((NBUF - 2) * kCopiesPerTile < 64, "vmcnt range");
     constexpr int KS = D / 16, DB = D / 32;
@@ -239,12 +240,19 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
     const uint32_t req_bytes = (uint32_t)((int64_t)Lr * HD * 2);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, req_bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, req_bytes);
-    auto dma = [&](int n0, auto S) __attribute__((always_inline)) {
+    // copy number c (K passes, then V passes) of the tile of keys n0 .. n0 + BN - 1 into stage S
+    auto copy = [&](int c, int n0, auto S) __attribute__((always_inline)) {
         const uint32_t toff = (uint32_t)min((int64_t)n0 * HD * 2, (int64_t)0x7fff0000);
+        if (c < kPassK) {
+            if (c * NW + wave < kInstrK) buffer_copy16_to_lds(kr, koff[c] + toff, k_lds(S) + (c * NW + wave) * 64);
+        } else {
+            const int p = c - kPassK;
+            if (p * NW + wave < kInstrV) buffer_copy16_to_lds(vr, voff[p] + toff, v_lds(S) + (p * NW + wave) * 64);
+        }
+    };
+    auto dma = [&](int n0, auto S) __attribute__((always_inline)) {
 #pragma unroll
-        for (int p = 0; p < kPassK; ++p) buffer_copy16_to_lds(kr, koff[p] + toff, k_lds(S) + (p * NW + wave) * 64);
-#pragma unroll
-        for (int p = 0; p < kPassV; ++p) buffer_copy16_to_lds(vr, voff[p] + toff, v_lds(S) + (p * NW + wave) * 64);
+        for (int c = 0; c < kCopiesPerTile; ++c) copy(c, n0, S);
     };
 
     const float cl2 = a.scale * 1.4426950408889634f;
@@ -276,12 +284,10 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
 
     // Scores of tile `it` in stage S and their softmax weights into pb (MAXONLY: the per-query
     // max only). MASK: the ragged last tile. INIT: the first tile sets m_ref.
-    auto score = [&](int it, auto S, auto mask, auto init, auto maxonly) __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask)::value;
-        constexpr bool INIT = decltype(init)::value;
-        constexpr bool MAXONLY = decltype(maxonly)::value;
-        // S^T = K Q^T, K fragments streamed per k16 step
-        f32x16 sc[NKB];
+    f32x16 sc[NKB];         // scores of the last tile whose MFMAs ran
+    // S^T = K Q^T for the tile in stage S into sc, K fragments streamed per k16 step
+    // hook(ks) runs before the MFMAs of k16 step ks (the copies of the next tile are spread there)
+    auto scores = [&](auto S, auto hook) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -294,6 +300,7 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
         });
         static_for<KS>([&](auto ks) {
             constexpr int cur = ks % (KPD + 1);
+            hook(ks);
             if constexpr (ks + KPD < KS) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
@@ -303,6 +310,13 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
             for (int kb = 0; kb < NKB; ++kb) sc[kb] = mfma_32x32x16_bf16(kf[cur][kb], qf[ks], sc[kb]);
             sched_fence();     // keeps the reads KPD steps ahead, not hoisted further (registers)
         });
+    };
+    // Softmax weights of tile `it` from sc into pb (MAXONLY: the per-query max only). MASK: the
+    // ragged last tile. INIT: the first tile sets m_ref.
+    auto softmax = [&](int it, auto mask, auto init, auto maxonly) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask)::value;
+        constexpr bool INIT = decltype(init)::value;
+        constexpr bool MAXONLY = decltype(maxonly)::value;
         if (MASK) mask_tile<NKB>(sc, Lr - it * BN, half);
         if constexpr (MAXONLY) {
             mx = fmaxf(mx, tile_max<NKB>(sc));
@@ -311,8 +325,13 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
             exp_tile<NKB>(sc, pb, l, cl2, -mref);
         }
     };
+    auto no_hook = [](auto) {};
+    auto score = [&](int it, auto S, auto mask, auto init, auto maxonly) __attribute__((always_inline)) {
+        scores(S, no_hook);
+        softmax(it, mask, init, maxonly);
+    };
     // O^T += V^T P^T for the tile in stage S with the weights in pb, V^T streamed per 32 dims
-    auto pv = [&](auto S) __attribute__((always_inline)) {
+    auto pv = [&](auto S, auto hook) __attribute__((always_inline)) {
         const char *vp = (const char *)v_lds(S) + v_lane;
         bf16x8 vf[VPD + 1][NKB][2];
         auto vload = [&](int db, int set) __attribute__((always_inline)) {
@@ -329,6 +348,7 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
         static_for<VPD>([&](auto db) { vload(db, db); });
         static_for<DB>([&](auto db) {
             constexpr int cur = db % (VPD + 1);
+            hook(db);
             if constexpr (db + VPD < DB) vload(db + VPD, (db + VPD) % (VPD + 1));
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -340,25 +360,36 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
     // One whole tile, nothing else in flight (the overflow redo)
     auto tile = [&](int it, auto S, auto mask, auto maxonly) __attribute__((always_inline)) {
         score(it, S, mask, std::false_type(), maxonly);
-        if constexpr (!decltype(maxonly)::value) pv(S);
+        if constexpr (!decltype(maxonly)::value) pv(S, no_hook);
         wait_vmcnt<0>();
         barrier_lds();
     };
     const std::true_type T;
     const std::false_type F;
 
-    // ---- main pass: copies run NBUF - 1 tiles ahead; the ragged last tile is masked ----
+    // ---- main pass ----
+    // The copies of tile it + 1 go out one per k16 step of tile it's scores, so the eight waves
+    // do not queue all their copies at once right after the barrier; the copy unit is fed while
+    // the MFMAs run. Each barrier waits for the whole next tile.
+    // COPYAT 0: all copies in the k16 steps of the scores; 1: in the 32-dim steps of PV; 2: split
+    constexpr int kInS = COPYAT == 0 ? kCopiesPerTile : COPYAT == 1 ? 0 : (kCopiesPerTile + 1) / 2;
+    constexpr int kInPv = kCopiesPerTile - kInS;
+    static_assert(kInS <= KS && (kInPv + DB - 1) / DB <= 2, "copy spreading");
     auto step = [&](int it, auto S, auto mask) __attribute__((always_inline)) {
-        // the stage of tile it + NBUF - 1 held tile it - 1, finished before the last barrier
-        dma((it + NBUF - 1) * BN, IC<(S + NBUF - 1) % NBUF>{});
-        score(it, S, mask, T, F);
-        pv(S);
-        wait_vmcnt<(NBUF - 2) * kCopiesPerTile>();     // tile it + 1 landed
+        scores(S, [&](auto ks) __attribute__((always_inline)) {
+            if constexpr (ks < kInS) copy(ks, (it + 1) * BN, IC<(S + 1) % NBUF>{});
+        });
+        softmax(it, mask, T, F);
+        pv(S, [&](auto db) __attribute__((always_inline)) {
+            if constexpr (db < kInPv) copy(kInS + db, (it + 1) * BN, IC<(S + 1) % NBUF>{});
+            if constexpr (db + DB < kInPv) copy(kInS + DB + db, (it + 1) * BN, IC<(S + 1) % NBUF>{});
+        });
+        wait_vmcnt<0>();     // tile it + 1 landed
         barrier_lds();
     };
     if (ntiles > 0) {
-        static_for<NBUF - 1>([&](auto S) { dma(S * BN, S); });
-        wait_vmcnt<(NBUF - 2) * kCopiesPerTile>();
+        dma(0, IC<0>{});
+        wait_vmcnt<0>();
         barrier_lds();
         const int nfull = ragged ? ntiles - 1 : ntiles;
         for (int it0 = 0; it0 < nfull; it0 += NBUF)
@@ -371,8 +402,6 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
                 if (st == S) step(ntiles - 1, S, T);
             });
         }
-        wait_vmcnt<0>();     // copies past the end (zeros) land before the stages are reused
-        barrier_lds();
     }
 
     // ---- overflow check and redo, one tile copied at a time ----
@@ -427,7 +456,7 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
 template <int D>
 struct DcaBf16Config {
     // 8 waves x 32 query rows, 64-key tiles, two LDS stages, K reads two k16 steps ahead
-    static constexpr int NW = 8, NKB = 2, NBUF = 2, KPD = 2, VPD = 1;
+    static constexpr int NW = 8, NKB = 2, NBUF = 2, KPD = 1, VPD = 1, COPYAT = 0;
     static constexpr int BM = NW * 32;
 };
 
@@ -533,11 +562,11 @@ hipError_t launch_dca(const DcaArgs &a, hipStream_t s) {
         hipLaunchKernelGGL(dca_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
     } else if (a.D == 128) {
         using C = DcaBf16Config<128>;
-        hipLaunchKernelGGL((dca_bf16_kernel<128, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((dca_bf16_kernel<128, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD, C::COPYAT>), dim3((unsigned)grid),
                            dim3(C::NW * 64), 0, s, a);
     } else if (a.D == 64) {
         using C = DcaBf16Config<64>;
-        hipLaunchKernelGGL((dca_bf16_kernel<64, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((dca_bf16_kernel<64, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD, C::COPYAT>), dim3((unsigned)grid),
                            dim3(C::NW * 64), 0, s, a);
     } else {
         return hipErrorInvalidValue;
