@@ -230,9 +230,12 @@ def main():
             tj = json.load(f)
         ent = tj.get(args.workload, {}).get(dominant)
         if ent:
-            with open(os.path.join(ROOT, ent["file"]), "rb") as f:
-                sha = hashlib.sha256(f.read()).hexdigest()[:16]
-            if sha == ent.get("source_sha256_prefix"):
+            # the kernel's sources, hashed together in the listed order
+            h = hashlib.sha256()
+            for name in ent["files"]:
+                with open(os.path.join(ROOT, name), "rb") as f:
+                    h.update(f.read())
+            if h.hexdigest()[:16] == ent.get("source_sha256_prefix"):
                 traffic = ent.get("bytes_per_launch")
     except (OSError, ValueError, KeyError):
         traffic = None

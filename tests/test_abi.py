@@ -84,6 +84,9 @@ def test_dca_argument_errors(lib):
     assert dca(lib, d=96) == ikbo.IKBO_UNSUPPORTED
     assert dca(lib, ind=0, d=130) == ikbo.IKBO_UNSUPPORTED
     assert dca(lib, ind=7) == ikbo.IKBO_UNSUPPORTED
+    # a request's bf16 K block must span fewer than 2^31 bytes: 1M keys x 8 heads x 128 x 2 B does not
+    assert dca(lib, L=1 << 20, H=8) == ikbo.IKBO_UNSUPPORTED
+    assert b"2^31" in lib.ikbo_last_error_message()
     assert dca(lib, q=MIS) == ikbo.IKBO_MISALIGNED
     assert dca(lib, m=MIS) == ikbo.IKBO_MISALIGNED
     assert dca(lib, q=None) == ikbo.IKBO_INVALID_ARGUMENT
