@@ -119,51 +119,40 @@ __device__ __forceinline__ float half_swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Masks keys at or past L_r in the last tile: s[kb][j] holds key kb*32 + 8*(j/4) + 4*half + j%4.
-template <int NKB>
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[NKB], int rem, int half) {
+// Masks the keys at or past `rem` of one 32-key block: s[j] holds key 8*(j/4) + 4*half + j%4.
+__device__ __forceinline__ void mask_block(f32x16 &s, int rem, int half) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-            if (kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3) >= rem) s[kb][j] = -INFINITY;
+    for (int j = 0; j < 16; ++j)
+        if (8 * (j >> 2) + 4 * half + (j & 3) >= rem) s[j] = -INFINITY;
 }
 
-// Max over the lane's scores of one tile, then over the two 32-lane halves (one query column).
-template <int NKB>
-__device__ __forceinline__ float tile_max(const f32x16 (&s)[NKB]) {
-    float mx = fmaxf(s[0][0], s[0][1]);
+// Max over the lane's scores of one 32-key block, then over the two 32-lane halves (one query).
+__device__ __forceinline__ float block_max(const f32x16 &s) {
+    float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int j = (kb == 0 ? 2 : 0); j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+    for (int j = 2; j < 16; ++j) mx = fmaxf(mx, s[j]);
     return half_swap_max(mx);
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// p = 2^(s * scale * log2(e) - m_ref) against a fixed per-query reference; packs the bf16 B
-// operands of the PV MFMAs and adds the packed (rounded) weights to the row sum, so the sum
-// normalises exactly the weights the PV MFMAs use.
-template <int NKB>
-__device__ __forceinline__ void exp_tile(f32x16 (&s)[NKB], bf16x8 (&pb)[NKB][2], float &l, float cl2, float mneg) {
+// p = 2^(s * scale * log2(e) - m_ref) for one 32-key block against a fixed per-query reference;
+// packs the bf16 B operands of the PV MFMAs and adds the packed (rounded) weights to the row sum,
+// so the sum normalises exactly the weights the PV MFMAs use.
+__device__ __forceinline__ void exp_block(f32x16 &s, bf16x8 (&pb)[2], float &l, float cl2, float mneg) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j], cl2, mneg));
+    for (int j = 0; j < 16; ++j) s[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], cl2, mneg));
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)s[8 * u + e];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[kb][u][e] = (__bf16)s[kb][8 * u + e];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const bf16x2 pr = {pb[kb][u][e], pb[kb][u][e + 1]};
-                l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
-            }
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pb[u][e], pb[u][e + 1]};
+            l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
         }
+    }
 }
 
 template <int D, int NW, int NKB, int NBUF, int KPD, int VPD, int COPYAT>
@@ -282,67 +271,75 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
 
     bf16x8 pb[NKB][2];      // bf16 weights of the last scored tile (B operands of the PV MFMAs)
 
-    // Scores of tile `it` in stage S and their softmax weights into pb (MAXONLY: the per-query
-    // max only). MASK: the ragged last tile. INIT: the first tile sets m_ref.
+    // The score / softmax / PV parts below act on the 32-key blocks kb in [KB0, KB1) of a tile.
     f32x16 sc[NKB];         // scores of the last tile whose MFMAs ran
-    // S^T = K Q^T for the tile in stage S into sc, K fragments streamed per k16 step
+    // S^T = K Q^T for the tile in stage S into sc, K fragments streamed per k16 step;
     // hook(ks) runs before the MFMAs of k16 step ks (the copies of the next tile are spread there)
-    auto scores = [&](auto S, auto hook) __attribute__((always_inline)) {
+    auto scores = [&](auto S, auto KB0, auto KB1, auto hook) __attribute__((always_inline)) {
+        constexpr int B0 = KB0, B1 = KB1, NB = B1 - B0;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = B0; kb < B1; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) sc[kb][j] = 0.0f;
         const uint4 *kp = k_lds(S) + k_lane;
-        bf16x8 kf[KPD + 1][NKB];     // KPD steps of reads in flight ahead of the MFMAs
+        bf16x8 kf[KPD + 1][NB];      // KPD steps of reads in flight ahead of the MFMAs
         static_for<KPD>([&](auto ks) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) kf[ks][kb] = __builtin_bit_cast(bf16x8, kp[kb * 32 * KSR + ks * 2]);
+            for (int b = 0; b < NB; ++b) kf[ks][b] = __builtin_bit_cast(bf16x8, kp[(B0 + b) * 32 * KSR + ks * 2]);
         });
         static_for<KS>([&](auto ks) {
             constexpr int cur = ks % (KPD + 1);
             hook(ks);
             if constexpr (ks + KPD < KS) {
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-                    kf[(ks + KPD) % (KPD + 1)][kb] = __builtin_bit_cast(bf16x8, kp[kb * 32 * KSR + (ks + KPD) * 2]);
+                for (int b = 0; b < NB; ++b)
+                    kf[(ks + KPD) % (KPD + 1)][b] = __builtin_bit_cast(bf16x8, kp[(B0 + b) * 32 * KSR + (ks + KPD) * 2]);
             }
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) sc[kb] = mfma_32x32x16_bf16(kf[cur][kb], qf[ks], sc[kb]);
+            for (int b = 0; b < NB; ++b) sc[B0 + b] = mfma_32x32x16_bf16(kf[cur][b], qf[ks], sc[B0 + b]);
             sched_fence();     // keeps the reads KPD steps ahead, not hoisted further (registers)
         });
     };
     // Softmax weights of tile `it` from sc into pb (MAXONLY: the per-query max only). MASK: the
-    // ragged last tile. INIT: the first tile sets m_ref.
-    auto softmax = [&](int it, auto mask, auto init, auto maxonly) __attribute__((always_inline)) {
+    // ragged last tile. INIT: the first tile sets m_ref (a whole tile's blocks must be present).
+    auto softmax = [&](int it, auto KB0, auto KB1, auto mask, auto init, auto maxonly) __attribute__((always_inline)) {
+        constexpr int B0 = KB0, B1 = KB1;
         constexpr bool MASK = decltype(mask)::value;
         constexpr bool INIT = decltype(init)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
-        if (MASK) mask_tile<NKB>(sc, Lr - it * BN, half);
+        static_assert(!INIT || (B0 == 0 && B1 == NKB), "the reference is the max of a whole tile");
+#pragma unroll
+        for (int kb = B0; kb < B1; ++kb)
+            if (MASK) mask_block(sc[kb], Lr - it * BN - kb * 32, half);
         if constexpr (MAXONLY) {
-            mx = fmaxf(mx, tile_max<NKB>(sc));
+#pragma unroll
+            for (int kb = B0; kb < B1; ++kb) mx = fmaxf(mx, block_max(sc[kb]));
         } else {
-            if (INIT && it == 0) mref = tile_max<NKB>(sc) * cl2;
-            exp_tile<NKB>(sc, pb, l, cl2, -mref);
+            if (INIT && it == 0) {
+                float m0 = block_max(sc[0]);
+#pragma unroll
+                for (int kb = 1; kb < NKB; ++kb) m0 = fmaxf(m0, block_max(sc[kb]));
+                mref = m0 * cl2;
+            }
+#pragma unroll
+            for (int kb = B0; kb < B1; ++kb) exp_block(sc[kb], pb[kb], l, cl2, -mref);
         }
     };
     auto no_hook = [](auto) {};
-    auto score = [&](int it, auto S, auto mask, auto init, auto maxonly) __attribute__((always_inline)) {
-        scores(S, no_hook);
-        softmax(it, mask, init, maxonly);
-    };
     // O^T += V^T P^T for the tile in stage S with the weights in pb, V^T streamed per 32 dims
-    auto pv = [&](auto S, auto hook) __attribute__((always_inline)) {
+    auto pv = [&](auto S, auto KB0, auto KB1, auto hook) __attribute__((always_inline)) {
+        constexpr int B0 = KB0, B1 = KB1, NB = B1 - B0;
         const char *vp = (const char *)v_lds(S) + v_lane;
-        bf16x8 vf[VPD + 1][NKB][2];
+        bf16x8 vf[VPD + 1][NB][2];
         auto vload = [&](int db, int set) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const int o0 = (kb * 32 + 16 * u) * VROW + db * 64;
+                    const int o0 = ((B0 + b) * 32 + 16 * u) * VROW + db * 64;
                     i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + o0));
                     i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + o0 + 8 * VROW));
-                    vf[set][kb][u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    vf[set][b][u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
         };
         static_for<VPD>([&](auto db) { vload(db, db); });
@@ -351,16 +348,22 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
             hook(db);
             if constexpr (db + VPD < DB) vload(db + VPD, (db + VPD) % (VPD + 1));
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) o[db] = mfma_32x32x16_bf16(vf[cur][kb][u], pb[kb][u], o[db]);
+                for (int u = 0; u < 2; ++u) o[db] = mfma_32x32x16_bf16(vf[cur][b][u], pb[B0 + b][u], o[db]);
             sched_fence();
         });
+    };
+    const IC<0> K0;
+    const IC<NKB> KN;
+    auto score = [&](int it, auto S, auto mask, auto init, auto maxonly) __attribute__((always_inline)) {
+        scores(S, K0, KN, no_hook);
+        softmax(it, K0, KN, mask, init, maxonly);
     };
     // One whole tile, nothing else in flight (the overflow redo)
     auto tile = [&](int it, auto S, auto mask, auto maxonly) __attribute__((always_inline)) {
         score(it, S, mask, std::false_type(), maxonly);
-        if constexpr (!decltype(maxonly)::value) pv(S, no_hook);
+        if constexpr (!decltype(maxonly)::value) pv(S, K0, KN, no_hook);
         wait_vmcnt<0>();
         barrier_lds();
     };
@@ -376,14 +379,16 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
     constexpr int kInPv = kCopiesPerTile - kInS;
     static_assert(kInS <= KS && (kInPv + DB - 1) / DB <= 2, "copy spreading");
     auto step = [&](int it, auto S, auto mask) __attribute__((always_inline)) {
-        scores(S, [&](auto ks) __attribute__((always_inline)) {
+        auto copies_s = [&](auto ks) __attribute__((always_inline)) {
             if constexpr (ks < kInS) copy(ks, (it + 1) * BN, IC<(S + 1) % NBUF>{});
-        });
-        softmax(it, mask, T, F);
-        pv(S, [&](auto db) __attribute__((always_inline)) {
+        };
+        auto copies_pv = [&](auto db) __attribute__((always_inline)) {
             if constexpr (db < kInPv) copy(kInS + db, (it + 1) * BN, IC<(S + 1) % NBUF>{});
             if constexpr (db + DB < kInPv) copy(kInS + DB + db, (it + 1) * BN, IC<(S + 1) % NBUF>{});
-        });
+        };
+        scores(S, K0, KN, copies_s);
+        softmax(it, K0, KN, mask, T, F);
+        pv(S, K0, KN, copies_pv);
         wait_vmcnt<0>();     // tile it + 1 landed
         barrier_lds();
     };
