@@ -113,13 +113,23 @@ __device__ __forceinline__ bool row_request(const GemmArgs &a, int64_t row, int6
 template <int CPR>
 __device__ __forceinline__ int swzc(int row) { return CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
 
-template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL>
-__global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t tiles_m, int32_t tiles_n,
-                                                            int32_t k_per_split) {
-    constexpr int T = WGM * WGN * 64;
-    constexpr int TBM = WGM * TM, TBN = WGN * TN;
-    constexpr int CPR = TBK / 8;                       // 16-byte chunks per tile row
-    constexpr int XCH = TBM * CPR, WCH = TBN * CPR;    // chunks per X / W tile
+// Tile geometry of a bf16 GEMM configuration.
+template <int WGM, int WGN, int TM, int TN, int TBK>
+struct GemmShape {
+    static constexpr int T = WGM * WGN * 64;
+    static constexpr int TBM = WGM * TM, TBN = WGN * TN;
+    static constexpr int CPR = TBK / 8;                       // 16-byte chunks per tile row
+    static constexpr int XCH = TBM * CPR, WCH = TBN * CPR;    // chunks per X / W tile
+};
+
+// One output tile (mt, nt) over the k range of split sp. sx[s] / sw[s] are the LDS stages of the
+// activation / weight tiles (the caller's __shared__ arrays, one per stage). pre_epilogue() runs
+// between the main loop and the epilogue.
+template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL, typename Pre>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int sp, int32_t k_per_split,
+                                          uint4 *const *sx, uint4 *const *sw, Pre pre_epilogue) {
+    using G = GemmShape<WGM, WGN, TM, TN, TBK>;
+    constexpr int T = G::T, TBM = G::TBM, TBN = G::TBN, CPR = G::CPR, XCH = G::XCH, WCH = G::WCH;
     constexpr int XP = XCH / T, WP = WCH / T;          // load passes
     static_assert(XCH % T == 0 && WCH % T == 0, "tile load must split evenly");
     constexpr int MB = TM / 32, NB = TN / 32;
@@ -128,31 +138,9 @@ __global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t
     constexpr uint32_t kOutOfRange = 0x80000000u;      // past every tile's buffer range (< 2^31 bytes)
     static_assert(NBUF <= 4 && (NBUF - 2) * kCopies < 64, "vmcnt range");
     static_assert(!DMA || (T / CPR) % 16 == 0, "direct copies: the chunk swizzle must repeat every pass");
+    auto xs = [&](auto S) -> uint4 * { return sx[decltype(S)::value]; };
+    auto ws = [&](auto S) -> uint4 * { return sw[decltype(S)::value]; };
 
-    // one LDS variable per stage: the compiler gives each its own alias scope, so reading one stage
-    // does not wait for copies still in flight into another
-    __shared__ uint4 sx0[XCH], sx1[XCH], sx2[NBUF > 2 ? XCH : 1], sx3[NBUF > 3 ? XCH : 1];
-    __shared__ uint4 sw0[WCH], sw1[WCH], sw2[NBUF > 2 ? WCH : 1], sw3[NBUF > 3 ? WCH : 1];
-    auto xs = [&](auto S) -> uint4 * {
-        if constexpr (decltype(S)::value == 0) return sx0;
-        else if constexpr (decltype(S)::value == 1) return sx1;
-        else if constexpr (decltype(S)::value == 2) return sx2;
-        else return sx3;
-    };
-    auto ws = [&](auto S) -> uint4 * {
-        if constexpr (decltype(S)::value == 0) return sw0;
-        else if constexpr (decltype(S)::value == 1) return sw1;
-        else if constexpr (decltype(S)::value == 2) return sw2;
-        else return sw3;
-    };
-
-    const int64_t total = (int64_t)tiles_m * tiles_n * a.splits;
-    int64_t t = xcd_tile(blockIdx.x, total);
-    if (t < 0) return;
-    const int nt = (int)(t % tiles_n);
-    t /= tiles_n;
-    const int mt = (int)(t % tiles_m);
-    const int sp = (int)(t / tiles_m);
     const int64_t m0 = (int64_t)mt * TBM;
     const int n0 = nt * TBN;
     const int kbeg = sp * k_per_split;
@@ -323,6 +311,8 @@ __global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t
         }
     }
 
+    pre_epilogue();
+
     // ---- epilogue ----
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
@@ -352,6 +342,29 @@ __global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t
                 }
         }
     }
+}
+
+// One LDS variable per stage: the compiler gives each its own alias scope, so reading one stage
+// does not wait for copies still in flight into another.
+#define IKBO_GEMM_LDS(G, NBUF)                                                                                         \
+    __shared__ uint4 sx0[G::XCH], sx1[G::XCH], sx2[NBUF > 2 ? G::XCH : 1], sx3[NBUF > 3 ? G::XCH : 1];              \
+    __shared__ uint4 sw0[G::WCH], sw1[G::WCH], sw2[NBUF > 2 ? G::WCH : 1], sw3[NBUF > 3 ? G::WCH : 1];              \
+    uint4 *const sx[4] = {sx0, sx1, sx2, sx3};                                                                      \
+    uint4 *const sw[4] = {sw0, sw1, sw2, sw3}
+
+template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL>
+__global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t tiles_m, int32_t tiles_n,
+                                                            int32_t k_per_split) {
+    using G = GemmShape<WGM, WGN, TM, TN, TBK>;
+    IKBO_GEMM_LDS(G, NBUF);
+    const int64_t total = (int64_t)tiles_m * tiles_n * a.splits;
+    int64_t t = xcd_tile(blockIdx.x, total);
+    if (t < 0) return;
+    const int nt = (int)(t % tiles_n);
+    t /= tiles_n;
+    const int mt = (int)(t % tiles_m);
+    const int sp = (int)(t / tiles_m);
+    gemm_tile<WGM, WGN, TM, TN, TBK, NBUF, DMA, PARTIAL>(a, mt, nt, sp, k_per_split, sx, sw, [] {});
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -419,21 +432,146 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int32_t tiles
     }
 }
 
+// One element of the split-K reduction: partials summed in split order, then the request-group
+// epilogue (columns below n_split) or the raw sum into Z.
+__device__ __forceinline__ void reduce_elem(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
+                                            const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1,
+                                            int64_t row, int32_t col) {
+    const int64_t total = M * N, i = row * N + col;
+    float s = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) s += partial[(int64_t)sp * total + i];
+    if (col < n_split) {
+        float v = s + (bias0 ? bias0[col] : 0.0f);
+        v = apply_act(act, v);
+        if (out0_f32) ((float *)out0)[row * n_split + col] = v;
+        else ((uint16_t *)out0)[row * n_split + col] = f32_to_bf16(v);
+    } else {
+        out1[row * (N - n_split) + (col - n_split)] = s;
+    }
+}
+
 __global__ void splitk_reduce_kernel(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
                                      const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1) {
     const int64_t total = M * N;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t row = i / N;
-        const int32_t col = (int32_t)(i - row * N);
-        float s = 0.0f;
-        for (int sp = 0; sp < splits; ++sp) s += partial[(int64_t)sp * total + i];
-        if (col < n_split) {
-            float v = s + (bias0 ? bias0[col] : 0.0f);
-            v = apply_act(act, v);
-            if (out0_f32) ((float *)out0)[row * n_split + col] = v;
-            else ((uint16_t *)out0)[row * n_split + col] = f32_to_bf16(v);
+        reduce_elem(partial, splits, M, N, n_split, bias0, act, out0, out0_f32, out1, row, (int32_t)(i - row * N));
+    }
+}
+
+// ----------------------------------------------------------------------------------------------
+// Persistent LCB layer (request/candidate co-scheduling, ROCS Sec. 4.2.3). sync layout (int32):
+// [0] request item counter, [1 .. 8] candidate tile counter of each XCD, [9] wait ran out,
+// [16 .. 16 + Q) arrivals per request tile, [16 + Q .. 16 + 2Q) ready flags (Q request tiles).
+constexpr int kSyncHead = 16;
+
+__device__ __forceinline__ int32_t flag_load_acquire(const int32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_store_release(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool DMA_R, bool DMA_C>
+__global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f) {
+    using G = GemmShape<kWGM, kWGN, kTM, kTN, BK>;
+    IKBO_GEMM_LDS(G, 2);
+    __shared__ int64_t s_item;
+    __shared__ int32_t s_last;
+    const int tid = threadIdx.x;
+    const int xcd = blockIdx.x % kNumXcd;
+    const GemmArgs &rq = f.req, &cd = f.cand;
+    const int32_t rtm = (int32_t)((rq.M + BM - 1) / BM), rtn = (rq.N + BN - 1) / BN;
+    const int32_t splits = rq.splits;
+    const int64_t req_tiles = (int64_t)rtm * rtn, req_items = req_tiles * splits;
+    const int32_t rkps = (int32_t)((((int64_t)rq.K + splits - 1) / splits + BK - 1) / BK * BK);
+    const int32_t ctn = (cd.N + BN - 1) / BN;
+    const int64_t cand_tiles = ((cd.M + BM - 1) / BM) * ctn;
+    const int64_t per_xcd = (cand_tiles + kNumXcd - 1) / kNumXcd;
+    const int64_t c_beg = xcd * per_xcd, c_end = min(cand_tiles, c_beg + per_xcd);
+    int32_t *arrive = f.sync + kSyncHead, *ready = f.sync + kSyncHead + req_tiles;
+
+    for (;;) {
+        if (tid == 0) {
+            int64_t item = -1;
+            const int64_t r = atomicAdd(&f.sync[0], 1);
+            if (r < req_items) {
+                item = r;
+            } else {
+                const int64_t c = c_beg + atomicAdd(&f.sync[1 + xcd], 1);
+                if (c < c_end) item = req_items + c;
+            }
+            s_item = item;
+        }
+        __syncthreads();
+        const int64_t item = s_item;
+        __syncthreads();
+        if (item < 0) break;
+        if (item < req_items) {
+            // request tile, one k split; splits of a tile are consecutive items
+            const int64_t tile = item / splits;
+            const int sp = (int)(item % splits);
+            const int mt = (int)(tile / rtn), nt = (int)(tile % rtn);
+            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_R, true>(rq, mt, nt, sp, rkps, sx, sw, [] {});
+            __threadfence();                       // the partials are visible device-wide ...
+            __syncthreads();
+            if (tid == 0) s_last = atomicAdd(&arrive[tile], 1) == splits - 1;    // ... before the arrival
+            __syncthreads();
+            if (s_last) {
+                __threadfence();                   // the other splits' partials
+                const int64_t m0 = (int64_t)mt * BM;
+                const int n0 = nt * BN;
+                for (int i = tid; i < BM * BN; i += kGemmThreads) {
+                    const int64_t row = m0 + i / BN;
+                    const int col = n0 + i % BN;
+                    if (row < rq.M && col < rq.N)
+                        reduce_elem(rq.partial, splits, rq.M, rq.N, f.n_split, f.bias0, f.act, f.out0, f.out0_f32,
+                                    const_cast<float *>(cd.z), row, col);
+                }
+                __threadfence();
+                __syncthreads();
+                if (tid == 0) flag_store_release(&ready[tile], 1);
+            }
         } else {
-            out1[row * (N - n_split) + (col - n_split)] = s;
+            const int64_t c = item - req_items;
+            const int mt = (int)(c / ctn), nt = (int)(c % ctn);
+            // request tiles holding Z columns nt * BN .. nt * BN + BN - 1 (all request row blocks)
+            auto wait_z = [&] {
+                if (tid == 0) {
+                    const int tn0 = (f.n_split + nt * BN) / BN;
+                    const int tn1 = min(rtn - 1, (f.n_split + min(cd.N, nt * BN + BN) - 1) / BN);
+                    // once any wait has run out, later tiles do not wait again
+                    bool ok = flag_load_acquire(&f.sync[9]) == 0;
+                    for (int tm = 0; tm < rtm && ok; ++tm)
+                        for (int tn = tn0; tn <= tn1 && ok; ++tn) {
+                            int64_t spins = 0;
+                            while (flag_load_acquire(&ready[(int64_t)tm * rtn + tn]) == 0) {
+                                if (++spins > f.spin_limit) {
+                                    ok = false;
+                                    atomicExch(&f.sync[9], 1);
+                                    break;
+                                }
+                                __builtin_amdgcn_s_sleep(2);
+                            }
+                        }
+                    s_last = ok;
+                }
+                __syncthreads();
+                __threadfence();                   // acquire for every thread's Z reads
+            };
+            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_C, false>(cd, mt, nt, 0, cd.K, sx, sw, wait_z);
+            if (!s_last) {
+                // the wait ran out: mark the tile's rows as invalid output
+                for (int i = tid; i < BM * BN; i += kGemmThreads) {
+                    const int64_t row = (int64_t)mt * BM + i / BN;
+                    const int col = nt * BN + i % BN;
+                    if (row < cd.M && col < cd.N) {
+                        if (cd.out_f32) ((float *)cd.out)[row * cd.ldo + col] = __builtin_nanf("");
+                        else ((uint16_t *)cd.out)[row * cd.ldo + col] = 0x7fc0;
+                    }
+                }
+            }
+            __syncthreads();
         }
     }
 }
@@ -450,6 +588,19 @@ int32_t request_gemm_splits(int64_t M, int32_t N, int32_t K, int in_f32) {
     if (s > 16) s = 16;
     if (s < 1) s = 1;
     return (int32_t)s;
+}
+
+// the direct-copy conditions of launch_gemm for one bf16 GEMM with k split kps
+static bool gemm_dma_ok(const GemmArgs &a, int32_t kps) {
+    return a.K % BK == 0 && kps % BK == 0 && a.ldx % 8 == 0 && ((uintptr_t)a.x & 15) == 0 &&
+           ((uintptr_t)a.w0 & 15) == 0 && ((uintptr_t)a.w1 & 15) == 0 && (a.n0 >= a.N || a.n0 % BN == 0) &&
+           (int64_t)BM * a.ldx * 2 < (1LL << 31) && (int64_t)BN * a.K * 2 < (1LL << 31);
+}
+
+static int32_t k_per_split(const GemmArgs &a) {
+    const int splits = a.partial ? (a.splits > 0 ? a.splits : 1) : 1;
+    int32_t kps = (int32_t)((((int64_t)a.K + splits - 1) / splits + BK - 1) / BK * BK);
+    return kps <= 0 ? BK : kps;
 }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
@@ -470,10 +621,7 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
     } else {
         // direct copies: k tiles whole, 16-byte aligned rows, buffer ranges within 32 bits, and no
         // tile across the w0 / w1 boundary
-        const bool dma = a.K % BK == 0 && kps % BK == 0 && a.ldx % 8 == 0 && ((uintptr_t)a.x & 15) == 0 &&
-                         ((uintptr_t)a.w0 & 15) == 0 && ((uintptr_t)a.w1 & 15) == 0 &&
-                         (a.n0 >= a.N || a.n0 % BN == 0) && (int64_t)BM * a.ldx * 2 < (1LL << 31) &&
-                         (int64_t)BN * a.K * 2 < (1LL << 31);
+        const bool dma = gemm_dma_ok(a, kps);
 #define IKBO_GEMM(D, P)                                                                                              \
     hipLaunchKernelGGL((gemm_bf16_t<kWGM, kWGN, kTM, kTN, BK, 2, D, P>), dim3((unsigned)grid), dim3(kGemmThreads), 0, \
                        s, b, (int32_t)tm, (int32_t)tn, kps)
@@ -486,6 +634,36 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
         }
 #undef IKBO_GEMM
     }
+    return hipGetLastError();
+}
+
+int64_t lcb_fused_sync_ints(int64_t M, int32_t N) {
+    return kSyncHead + 2 * ((M + BM - 1) / BM) * (int64_t)((N + BN - 1) / BN);
+}
+
+bool lcb_fused_supported(const GemmArgs &req, const GemmArgs &cand) {
+    return !req.in_f32 && !cand.in_f32 && req.partial && req.splits >= 1 && req.M > 0 && cand.M > 0 &&
+           req.N > 0 && cand.N > 0 && gemm_dma_ok(req, k_per_split(req)) && gemm_dma_ok(cand, cand.K);
+}
+
+hipError_t launch_lcb_fused(const LcbFusedArgs &f, hipStream_t s) {
+    if (!lcb_fused_supported(f.req, f.cand)) return hipErrorInvalidValue;
+    const int64_t nsync = lcb_fused_sync_ints(f.req.M, f.req.N);
+    hipError_t e = launch_fill_i32(f.sync, nsync, 0, s);
+    if (e != hipSuccess) return e;
+    static int cus = 0;
+    if (cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    // one workgroup per CU (the LDS stages take 128 KiB), a multiple of the XCD count
+    const int64_t items = (int64_t)((f.req.M + BM - 1) / BM) * ((f.req.N + BN - 1) / BN) * f.req.splits +
+                          ((f.cand.M + BM - 1) / BM) * ((f.cand.N + BN - 1) / BN);
+    int64_t grid = min((int64_t)cus, items);
+    grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
+    hipLaunchKernelGGL((lcb_fused_kernel<true, true>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, f);
     return hipGetLastError();
 }
 

@@ -80,4 +80,29 @@ hipError_t launch_splitk_reduce(const float *partial, int32_t splits, int64_t M,
 // Split count the request GEMM uses for an M x N x K problem.
 int32_t request_gemm_splits(int64_t M, int32_t N, int32_t K, int in_f32);
 
+// One persistent launch for an LCB layer (bf16): the request GEMM's split-K tiles are taken first
+// from a device-wide counter; the last split of a request tile to finish sums the partials in
+// split order and applies the request-group epilogue (out0 = act(sum + bias0) for columns below
+// n_split, Z = sum above), then releases that tile's ready flag. Candidate tiles are taken next
+// from one counter per XCD; each runs its main loop, then acquires the ready flags of the request
+// tiles holding its Z columns before the fused epilogue. Results equal launch_gemm +
+// launch_splitk_reduce + launch_gemm bit for bit.
+struct LcbFusedArgs {
+    GemmArgs req;           // request GEMM: partial = [splits][R][N] fp32, splits >= 1
+    GemmArgs cand;          // candidate GEMM: z = the request GEMM's Z output
+    int32_t n_split;        // request columns below n_split are Y_r, the rest Z
+    const float *bias0;
+    int32_t act;
+    void *out0;             // Y_r [R, n_split] or null when n_split == 0
+    int32_t out0_f32;
+    int32_t *sync;          // lcb_fused_sync_ints(...) int32, zeroed by launch_lcb_fused
+    int64_t spin_limit;     // bound on the flag wait (a wait that runs out sets sync[9] and poisons
+                            // the tile's output with NaN)
+};
+// int32 words of synchronisation state for a request GEMM of M rows and N columns
+int64_t lcb_fused_sync_ints(int64_t M, int32_t N);
+// whether launch_lcb_fused supports these two GEMMs (bf16 with direct copies)
+bool lcb_fused_supported(const GemmArgs &req, const GemmArgs &cand);
+hipError_t launch_lcb_fused(const LcbFusedArgs &f, hipStream_t s);
+
 }  // namespace ikbo
