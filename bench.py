@@ -243,6 +243,23 @@ def main():
                 "frac": round(dk["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": dominant, "flops_per_launch": flops[dominant], "ms_per_launch": round(dk["ms_avg"], 4)}
 
+    # IKBO-LCB also has a persistent request/candidate launch (IKBO_LCB_FUSED=1, same bits); time it
+    # after the timed region, on the same inputs, for comparison
+    alt = None
+    if args.workload == "lcb":
+        os.environ["IKBO_LCB_FUSED"] = "1"
+        try:
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps + 1)]
+            for i in range(args.steps + 1):
+                step(ev[i])
+            torch.cuda.synchronize()
+            d = [ev[i][0].elapsed_time(ev[i][1]) for i in range(1, args.steps + 1)]
+            alt = {"lcb_persistent_launch_ms_avg": round(float(np.mean(d)), 4),
+                   "lcb_two_launches_ms_avg": round(per["lcb"]["ms_avg"], 4)}
+            log("persistent LCB launch: %.3f ms" % alt["lcb_persistent_launch_ms_avg"])
+        finally:
+            os.environ.pop("IKBO_LCB_FUSED", None)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, np)
@@ -255,6 +272,8 @@ def main():
         "parts": {k: {kk: round(vv, 4) for kk, vv in d.items()} for k, d in per.items()},
         "roofline": roofline, "cpu_baseline": cpu,
     }
+    if alt:
+        line["alternate_forms"] = alt
     print(json.dumps(line), flush=True)
 
 
@@ -304,10 +323,11 @@ def cpu_baseline(args, np):
         sample = "%d candidates of requests %s" % (len(cands), reqs)
     else:
         g = synth.glm_spec("lcb")
-        reqs = [0, 1, g.R // 2, g.R - 1]
-        n_per = args.cpu_sample // 4 if args.cpu_sample else 64
+        # ten requests spread over the batch, up to 1024 candidates each (about 10 s of oracle work)
+        reqs = sorted(set(np.linspace(0, g.R - 1, 10).astype(int).tolist()))
+        n_per = args.cpu_sample // len(reqs) if args.cpu_sample else 1024
         off = g.offsets
-        cands = np.concatenate([np.arange(off[r], off[r] + n_per) for r in reqs]).astype(np.int64)
+        cands = np.concatenate([np.arange(off[r], min(off[r] + n_per, off[r + 1])) for r in reqs]).astype(np.int64)
         x_r, x_c = synth.glm_x(g, "x_r"), synth.glm_x(g, "x_c")
         ly = dict(synth.glm_weights(g, 0), act="gelu")
         t0 = time.perf_counter()

@@ -132,13 +132,12 @@ int run_lcb(const void *x_req, int64_t R, int32_t k_req, const void *x_cand, int
             void *y_req, void *y_cand, const LcbWs &ws, hipStream_t s) {
     const int in_f32 = in_dtype == IKBO_F32;
     const bool want_req = y_req != nullptr && n_req > 0;
-    // bf16 with both GEMMs on direct copies: one persistent launch that co-schedules the request
-    // tiles and the candidate tiles (Sec. 4.2.3). Switched off: its first run on the GPU did not
-    // finish (the candidate tiles never saw the request tiles' ready flags, although the claim /
-    // arrival / flag protocol completes in a host emulation), and the cause is not found yet.
-    // kLcbFusedEnabled stays false until it is; the two launches below are used.
-    constexpr bool kLcbFusedEnabled = false;
-    if (kLcbFusedEnabled && R > 0 && C > 0 && n_cand > 0 && !in_f32 && !getenv_flag("IKBO_LCB_TWO_LAUNCH")) {
+    // bf16 with both GEMMs on direct copies, IKBO_LCB_FUSED=1: one persistent launch that
+    // co-schedules the request tiles and the candidate tiles (Sec. 4.2.3). Its results equal the
+    // two launches below bit for bit; on this part the two launches are faster (the split-K
+    // request GEMM already fills the GPU for its few microseconds, and the persistent loop adds a
+    // claim and a flag check per tile), so they are the default.
+    if (R > 0 && C > 0 && n_cand > 0 && !in_f32 && getenv_flag("IKBO_LCB_FUSED")) {
         ikbo::LcbFusedArgs f = {};
         ikbo::GemmArgs &g = f.req;
         g.x = x_req;
@@ -178,7 +177,7 @@ int run_lcb(const void *x_req, int64_t R, int32_t k_req, const void *x_cand, int
         f.out0 = y_req;
         f.out0_f32 = out_dtype == IKBO_F32;
         f.sync = ws.sync;
-        f.spin_limit = 1LL << 24;     // ~1 s: a safety bound, never reached when the request tiles run
+        f.wait_ticks = ikbo::wall_clock_ticks(0.5);   // a safety bound, never reached when the request tiles run
         if ((size_t)R * (size_t)g.N <= ws.partial_cap && ws.sync_cap >= ikbo::lcb_fused_sync_ints(R, g.N) &&
             ikbo::lcb_fused_supported(g, h)) {
             IKBO_HIP(ikbo::launch_lcb_fused(f, s));

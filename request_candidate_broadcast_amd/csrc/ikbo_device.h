@@ -31,8 +31,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// GELU, exact form x * Phi(x) = x/2 (1 + erf(x / sqrt 2)).
-__device__ __forceinline__ float gelu_exact(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// GELU, exact form x Phi(x) = x/2 (1 + erf(x / sqrt 2)), with erf from the rational approximation of
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26: for u >= 0,
+// erf(u) = 1 - t P(t) exp(-u^2), t = 1 / (1 + p u), P(t) = a1 + a2 t + a3 t^2 + a4 t^3 + a5 t^4, with
+// |error| <= 1.5e-7. With u = |x| / sqrt 2 both signs of x give
+//   GELU(x) = max(x, 0) - |x| t (P(t) / 2) exp(-x^2 / 2),
+// which needs no 1 + erf (that sum loses the small tail for negative x) and no branch: one
+// reciprocal, one exp2 and a dozen FMA-class operations, where the library erff spends several
+// times that on range reduction and branches (GELU is the larger part of the GEMM epilogues).
+// |x| is capped at the largest float in the product so that GELU(+-inf) = +inf / 0; a NaN input
+// reaches the result through t. The cap and max(x, 0) are integer min / max on the bit patterns
+// (for floats >= 0 the integer order is the float order; a signed max with 0 maps every negative
+// float to +0), which needs none of the NaN-quieting the float min / max carry.
+__device__ __forceinline__ float gelu_exact(float x) {
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.23164188769779495f, ax, 1.0f));   // p / sqrt 2
+    float q = __builtin_fmaf(0.5307027145f, t, -0.7265760135f);                               // a5 / 2, a4 / 2
+    q = __builtin_fmaf(q, t, 0.7107068705f);                                                  // a3 / 2
+    q = __builtin_fmaf(q, t, -0.142248368f);                                                  // a2 / 2
+    q = __builtin_fmaf(q, t, 0.127414796f);                                                   // a1 / 2
+    const float axm = __uint_as_float(min(__float_as_uint(ax), 0x7f7fffffu));
+    const float h = (axm * t) * q;
+    const float e = __builtin_amdgcn_exp2f((x * x) * -0.72134752044448170f);                  // exp(-x^2 / 2)
+    const float relu = __int_as_float(max(__float_as_int(x), 0));
+    return __builtin_fmaf(-h, e, relu);
+}
 
 __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -31,9 +31,22 @@ constexpr int kGemmThreads = kWGM * kWGN * 64;
 
 __device__ __forceinline__ float apply_act(int act, float x) { return act == 1 ? gelu_exact(x) : x; }
 
-// Epilogue for 4 consecutive columns col..col+3 of one row.
+// A float read past the XCD's L2 (agent-coherent), for data other XCDs wrote during this launch.
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Epilogue for 4 consecutive columns col..col+3 of one row. ZCOH: Z was written during this launch
+// by other workgroups (it is read only after the flags of the request tiles holding its columns are
+// set). When every 128-byte line of Z holds columns of one 256-column request tile only (row
+// stride a multiple of 32 floats, Z 128-byte aligned), no line can reach this XCD's caches before
+// its final values (caches start the launch invalidated) and plain loads read them. Otherwise a
+// line can also hold columns of a tile not yet final when it is first read, and Z is read with
+// agent-coherent loads, past the L2.
+template <bool ZCOH = false>
 __device__ __forceinline__ void epilogue4(const GemmArgs &a, int64_t row, int64_t zrow, bool row_ok, int64_t col,
                                           float v0, float v1, float v2, float v3) {
+    const bool zcoh = ZCOH && ((a.ldz & 31) != 0 || ((uintptr_t)a.z & 127) != 0);
     float v[4] = {v0, v1, v2, v3};
     const bool full = col + 3 < a.N;
     if (!row_ok) {
@@ -51,11 +64,19 @@ __device__ __forceinline__ void epilogue4(const GemmArgs &a, int64_t row, int64_
         if (a.z) {
             const float *zp = a.z + zrow * a.ldz + col;
             if (full && (a.ldz & 3) == 0) {
-                const float4 zz = *(const float4 *)zp;
-                v[0] += zz.x; v[1] += zz.y; v[2] += zz.z; v[3] += zz.w;
+                if (zcoh) {
+                    const uint64_t *zq = (const uint64_t *)zp;
+                    const uint64_t lo = __hip_atomic_load(zq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint64_t hi = __hip_atomic_load(zq + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    v[0] += __uint_as_float((uint32_t)lo); v[1] += __uint_as_float((uint32_t)(lo >> 32));
+                    v[2] += __uint_as_float((uint32_t)hi); v[3] += __uint_as_float((uint32_t)(hi >> 32));
+                } else {
+                    const float4 zz = *(const float4 *)zp;
+                    v[0] += zz.x; v[1] += zz.y; v[2] += zz.z; v[3] += zz.w;
+                }
             } else {
                 for (int e = 0; e < 4; ++e)
-                    if (col + e < a.N) v[e] += zp[e];
+                    if (col + e < a.N) v[e] += zcoh ? load_coherent(zp + e) : zp[e];
             }
         }
         if (a.act) {
@@ -122,12 +143,86 @@ struct GemmShape {
     static constexpr int XCH = TBM * CPR, WCH = TBN * CPR;    // chunks per X / W tile
 };
 
+constexpr uint32_t kOutOfRange = 0x80000000u;      // past every tile's buffer range (< 2^31 bytes)
+
+// Direct-copy state of one output tile: buffer resources over its activation and weight rows (rows
+// past M / N read as zeros), this lane's byte offset in each (pass p adds p * T / CPR rows), and
+// its k tiles (nk from kbeg, visited from krot on, wrapping).
+struct DmaTile {
+    __amdgpu_buffer_rsrc_t xr, wr;
+    uint32_t xvoff, wvoff;
+    int nk, krot, kbeg;
+};
+
+// k tiles of split sp, and the first one visited. The N tiles that share a block of activation rows
+// run side by side on one XCD; starting each one k tile further along (nt mod 4) staggers them, so
+// one of them misses L2 on a given activation tile and the others find it there, instead of all of
+// them waiting on the same miss.
+template <int TBK>
+__device__ __forceinline__ void k_range(const GemmArgs &a, int nt, int sp, int32_t k_per_split, int &kbeg, int &kend,
+                                        int &nk, int &krot) {
+    kbeg = sp * k_per_split;
+    kend = min(a.K, kbeg + k_per_split);
+    nk = kend > kbeg ? (kend - kbeg + TBK - 1) / TBK : 0;
+    krot = nk > 0 ? (nt & 3) % nk : 0;
+}
+
+template <class G, int TBK>
+__device__ __forceinline__ DmaTile dma_tile(const GemmArgs &a, int mt, int nt, int sp, int32_t k_per_split, int wave,
+                                            int lane) {
+    constexpr int TBM = G::TBM, TBN = G::TBN, CPR = G::CPR;
+    DmaTile t;
+    int kend;
+    k_range<TBK>(a, nt, sp, k_per_split, t.kbeg, kend, t.nk, t.krot);
+    const int64_t m0 = (int64_t)mt * TBM;
+    const int n0 = nt * TBN;
+    const int row = (wave * 64 + lane) / CPR;
+    const int ch = (lane % CPR) ^ swzc<CPR>(row);
+    const int64_t mrows = min((int64_t)TBM, a.M - m0);
+    t.xr = make_rsrc((const uint16_t *)a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx * 2));
+    t.xvoff = (uint32_t)(row * a.ldx + ch * 8) * 2;
+    const bool second = n0 >= a.n0;     // a tile never straddles the w0 / w1 boundary here
+    const int nend = second ? a.N : min(a.N, a.n0);
+    const uint16_t *wbase = second ? (const uint16_t *)a.w1 + (int64_t)(n0 - a.n0) * a.K
+                                   : (const uint16_t *)a.w0 + (int64_t)n0 * a.K;
+    t.wr = make_rsrc(wbase, (uint32_t)(min(TBN, nend - n0) * a.K * 2));
+    t.wvoff = (uint32_t)(row * a.K + ch * 8) * 2;
+    return t;
+}
+
+// Copies step kt of a tile into one LDS stage (xs / ws); steps at or past nk read out of range.
+template <class G, int TBK>
+__device__ __forceinline__ void dma_fetch(const GemmArgs &a, const DmaTile &t, int kt, uint4 *xs, uint4 *ws, int wave) {
+    constexpr int T = G::T, CPR = G::CPR, XP = G::XCH / T, WP = G::WCH / T;
+    int ktr = kt + t.krot;
+    if (ktr >= t.nk) ktr -= t.nk;
+    const int k0 = t.kbeg + ktr * TBK;
+    const bool in = kt < t.nk;
+#pragma unroll
+    for (int p = 0; p < XP; ++p)
+        buffer_copy16_to_lds(t.xr, in ? t.xvoff + (uint32_t)(p * (T / CPR) * a.ldx + k0) * 2 : kOutOfRange,
+                             xs + p * T + wave * 64);
+#pragma unroll
+    for (int p = 0; p < WP; ++p)
+        buffer_copy16_to_lds(t.wr, in ? t.wvoff + (uint32_t)(p * (T / CPR) * a.K + k0) * 2 : kOutOfRange,
+                             ws + p * T + wave * 64);
+}
+
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
 // One output tile (mt, nt) over the k range of split sp. sx[s] / sw[s] are the LDS stages of the
 // activation / weight tiles (the caller's __shared__ arrays, one per stage). pre_epilogue() runs
-// between the main loop and the epilogue.
-template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL, typename Pre>
+// between the main loop and the epilogue (every thread), mid_epilogue() once inside the epilogue,
+// after the loads of its first column group are issued (LDS is free by then: a copy issued there
+// does not delay those loads, which it would when issued before them). prefetched: the caller has
+// already copied step 0 into stage 0 with dma_fetch (direct copies, two stages).
+template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL, bool ZCOH, typename Pre,
+          typename Mid = NoHook>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int sp, int32_t k_per_split,
-                                          uint4 *const *sx, uint4 *const *sw, Pre pre_epilogue) {
+                                          uint4 *const *sx, uint4 *const *sw, Pre pre_epilogue,
+                                          bool prefetched = false, Mid mid_epilogue = Mid()) {
     using G = GemmShape<WGM, WGN, TM, TN, TBK>;
     constexpr int T = G::T, TBM = G::TBM, TBN = G::TBN, CPR = G::CPR, XCH = G::XCH, WCH = G::WCH;
     constexpr int XP = XCH / T, WP = WCH / T;          // load passes
@@ -135,7 +230,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
     constexpr int MB = TM / 32, NB = TN / 32;
     constexpr int kCopies = XP + WP;
     static_assert(NBUF == 2 || DMA, "more than two stages need the direct copies");
-    constexpr uint32_t kOutOfRange = 0x80000000u;      // past every tile's buffer range (< 2^31 bytes)
     static_assert(NBUF <= 4 && (NBUF - 2) * kCopies < 64, "vmcnt range");
     static_assert(!DMA || (T / CPR) % 16 == 0, "direct copies: the chunk swizzle must repeat every pass");
     auto xs = [&](auto S) -> uint4 * { return sx[decltype(S)::value]; };
@@ -143,13 +237,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
 
     const int64_t m0 = (int64_t)mt * TBM;
     const int n0 = nt * TBN;
-    const int kbeg = sp * k_per_split;
-    const int kend = min(a.K, kbeg + k_per_split);
-    const int nk = kend > kbeg ? (kend - kbeg + TBK - 1) / TBK : 0;
-    // The N tiles that share a block of activation rows run side by side on one XCD. Starting each
-    // one k tile further along (nt mod 4) staggers them: one of them misses L2 on a given activation
-    // tile and the others find it there, instead of all of them waiting on the same miss.
-    const int krot = nk > 0 ? (nt & 3) % nk : 0;
+    int kbeg, kend, nk, krot;
+    k_range<TBK>(a, nt, sp, k_per_split, kbeg, kend, nk, krot);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // uniform: LDS copy bases in SGPRs
@@ -162,22 +251,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
     const uint16_t *xsrc[NP];
     const uint16_t *wsrc[NP];
     int xslot[NP], wslot[NP];
-    // Direct path: buffer resources over this tile's rows, so rows past M / N read as zeros, and one
-    // byte offset per operand and lane; pass p adds p * T / CPR rows.
-    __amdgpu_buffer_rsrc_t xr, wr;
-    uint32_t xvoff = 0, wvoff = 0;
+    // Direct path: the tile's buffer resources and lane offsets.
+    DmaTile dt;
     if constexpr (DMA) {
-        const int row = (wave * 64 + lane) / CPR;
-        const int ch = (lane % CPR) ^ swzc<CPR>(row);
-        const int64_t mrows = min((int64_t)TBM, a.M - m0);
-        xr = make_rsrc((const uint16_t *)a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx * 2));
-        xvoff = (uint32_t)(row * a.ldx + ch * 8) * 2;
-        const bool second = n0 >= a.n0;     // a tile never straddles the w0 / w1 boundary here
-        const int nend = second ? a.N : min(a.N, a.n0);
-        const uint16_t *wbase = second ? (const uint16_t *)a.w1 + (int64_t)(n0 - a.n0) * a.K
-                                       : (const uint16_t *)a.w0 + (int64_t)n0 * a.K;
-        wr = make_rsrc(wbase, (uint32_t)(min(TBN, nend - n0) * a.K * 2));
-        wvoff = (uint32_t)(row * a.K + ch * 8) * 2;
+        dt = dma_tile<G, TBK>(a, mt, nt, sp, k_per_split, wave, lane);
     } else {
 #pragma unroll
         for (int p = 0; p < XP; ++p) {
@@ -202,20 +279,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
     }
     uint4 px[NP], pw[NP];
     auto fetch = [&](int kt, auto st) {
-        int ktr = kt + krot;     // rotated k order, see krot
-        if (ktr >= nk) ktr -= nk;
-        const int k0 = kbeg + ktr * TBK;
         if constexpr (DMA) {
-            const bool in = kt < nk;
-#pragma unroll
-            for (int p = 0; p < XP; ++p)
-                buffer_copy16_to_lds(xr, in ? xvoff + (uint32_t)(p * (T / CPR) * a.ldx + k0) * 2 : kOutOfRange,
-                                     xs(st) + p * T + wave * 64);
-#pragma unroll
-            for (int p = 0; p < WP; ++p)
-                buffer_copy16_to_lds(wr, in ? wvoff + (uint32_t)(p * (T / CPR) * a.K + k0) * 2 : kOutOfRange,
-                                     ws(st) + p * T + wave * 64);
+            dma_fetch<G, TBK>(a, dt, kt, xs(st), ws(st), wave);
         } else {
+            int ktr = kt + krot;     // rotated k order, see k_range
+            if (ktr >= nk) ktr -= nk;
+            const int k0 = kbeg + ktr * TBK;
 #pragma unroll
             for (int p = 0; p < XP; ++p) {
                 const int ch = (tid + p * T) % CPR;
@@ -279,7 +348,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
         // Every step copies one tile. Tiles at or past nk are read out of range (zeros, no memory
         // access), so the loop has no data-dependent branch and a fixed number of copies in flight;
         // it runs to a multiple of NBUF steps, the extra ones multiplying zeros.
-        static_for<NBUF - 1>([&](auto S) { fetch(S, S); });
+        if (!prefetched) static_for<NBUF - 1>([&](auto S) { fetch(S, S); });
+        else static_for<NBUF - 2>([&](auto S) { fetch(S + 1, IC<S + 1>{}); });
         wait_vmcnt<(NBUF - 2) * kCopies>();                   // tile 0 landed
         barrier_lds();
         for (int base = 0; base < nk; base += NBUF) {
@@ -314,6 +384,149 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
     pre_epilogue();
 
     // ---- epilogue ----
+    // Fast form, uniform per tile: every column of the tile inside N and 16-byte output / Z rows.
+    // For each 32-column group i the bias and Z values of the lane's MB rows are loaded together
+    // before any of the group's results is stored, so a tile waits on NB load round trips instead
+    // of one per 4 columns (the stores may alias the loads, which keeps the compiler from moving
+    // loads past them). The branches on bias / Z / coherent reads are taken once per tile.
+    const int cw = n0 + wn * TN;     // first output column of this wave
+    const bool fast = n0 + TBN <= a.N &&
+                      (PARTIAL ? (a.N & 3) == 0 : ((a.ldo & 3) == 0 && (!a.z || (a.ldz & 3) == 0)));
+    if (fast) {
+        int64_t rowj[MB];
+        bool rin[MB];
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+            rowj[j] = m0 + wm * TM + j * 32 + l32;
+            rin[j] = rowj[j] < a.M;
+        }
+        if constexpr (PARTIAL) {
+            mid_epilogue();
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                if (!rin[j]) continue;
+                float *pp = a.partial + ((int64_t)sp * a.M + rowj[j]) * a.N + cw + 4 * half;
+#pragma unroll
+                for (int i = 0; i < NB; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        *(float4 *)(pp + i * 32 + 8 * jj) = make_float4(acc[i][j][4 * jj], acc[i][j][4 * jj + 1],
+                                                                        acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]);
+            }
+        } else {
+            // each row's request (rows whose request is out of range are written as zeros)
+            int64_t zoff[MB];
+            bool rok[MB];
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                bool ok = rin[j];
+                int64_t zr = 0;
+                if (a.z) {
+                    const int32_t r = rin[j] ? a.map[rowj[j]] : 0;
+                    ok = rin[j] && r >= 0 && r < a.R;
+                    zr = ok ? r : 0;
+                }
+                zoff[j] = zr * a.ldz;
+                rok[j] = ok;
+            }
+            const bool zcoh = ZCOH && a.z && ((a.ldz & 31) != 0 || ((uintptr_t)a.z & 127) != 0);
+            bool any_bad = false;
+#pragma unroll
+            for (int j = 0; j < MB; ++j) any_bad |= !rok[j];
+            const bool all_ok = __builtin_amdgcn_ballot_w64(any_bad) == 0;     // no row of the wave zeroed
+            // row bases: every access below is the base plus a compile-time offset
+            const float *zb[MB];
+            char *ob[MB];
+            const int osz = a.out_f32 ? 4 : 2;
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                zb[j] = a.z ? a.z + zoff[j] + cw + 4 * half : nullptr;
+                ob[j] = (char *)a.out + (rowj[j] * a.ldo + cw + 4 * half) * osz;
+            }
+            const float *bb = a.bias ? a.bias + cw + 4 * half : nullptr;
+            auto body = [&](auto HB, auto HZ, auto HC) __attribute__((always_inline)) {
+                static_for<NB>([&](auto I) __attribute__((always_inline)) {
+                    constexpr int i = decltype(I)::value;
+                    float4 bv[4], zv[MB][4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int c = i * 32 + 8 * jj;
+                        if constexpr (decltype(HB)::value) bv[jj] = *(const float4 *)(bb + c);
+                        else bv[jj] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                        for (int j = 0; j < MB; ++j) {
+                            if constexpr (!decltype(HZ)::value) {
+                                zv[j][jj] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                            } else if constexpr (decltype(HC)::value) {
+                                const uint64_t *zq = (const uint64_t *)(zb[j] + c);
+                                const uint64_t lo = __hip_atomic_load(zq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                const uint64_t hi = __hip_atomic_load(zq + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                zv[j][jj] = make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                                                        __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+                            } else {
+                                zv[j][jj] = *(const float4 *)(zb[j] + c);
+                            }
+                        }
+                    }
+                    if constexpr (i == 0) mid_epilogue();
+                    // pre-activation values of the group, then the activation (one branch per group)
+                    float v[MB][16];
+#pragma unroll
+                    for (int j = 0; j < MB; ++j)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            v[j][4 * jj + 0] = acc[i][j][4 * jj + 0] + bv[jj].x + zv[j][jj].x;
+                            v[j][4 * jj + 1] = acc[i][j][4 * jj + 1] + bv[jj].y + zv[j][jj].y;
+                            v[j][4 * jj + 2] = acc[i][j][4 * jj + 2] + bv[jj].z + zv[j][jj].z;
+                            v[j][4 * jj + 3] = acc[i][j][4 * jj + 3] + bv[jj].w + zv[j][jj].w;
+                        }
+                    if (a.act == 1) {
+#pragma unroll
+                        for (int j = 0; j < MB; ++j)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) v[j][e] = gelu_exact(v[j][e]);
+                    }
+                    if (!all_ok) {
+#pragma unroll
+                        for (int j = 0; j < MB; ++j)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) v[j][e] = rok[j] ? v[j][e] : 0.0f;
+                    }
+                    if (a.out_f32) {
+#pragma unroll
+                        for (int j = 0; j < MB; ++j)
+                            if (rin[j])
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj)
+                                    *(float4 *)(ob[j] + (i * 32 + 8 * jj) * 4) =
+                                        make_float4(v[j][4 * jj], v[j][4 * jj + 1], v[j][4 * jj + 2], v[j][4 * jj + 3]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < MB; ++j)
+                            if (rin[j])
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj)
+                                    *(uint2 *)(ob[j] + (i * 32 + 8 * jj) * 2) =
+                                        make_uint2(pack_bf16x2(v[j][4 * jj], v[j][4 * jj + 1]),
+                                                   pack_bf16x2(v[j][4 * jj + 2], v[j][4 * jj + 3]));
+                    }
+                });
+            };
+            const std::true_type T;
+            const std::false_type F;
+            if (a.bias) {
+                if (!a.z) body(T, F, F);
+                else if (zcoh) body(T, T, T);
+                else body(T, T, F);
+            } else {
+                if (!a.z) body(F, F, F);
+                else if (zcoh) body(F, T, T);
+                else body(F, T, F);
+            }
+        }
+        return;
+    }
+    mid_epilogue();
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
         const int64_t row = m0 + wm * TM + j * 32 + l32;
@@ -337,7 +550,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
                 for (int jj = 0; jj < 4; ++jj) {
                     const int64_t col = n0 + wn * TN + i * 32 + 8 * jj + 4 * half;
                     if (col < a.N)
-                        epilogue4(a, row, zrow, ok, col, acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
+                        epilogue4<ZCOH>(a, row, zrow, ok, col, acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2],
                                   acc[i][j][4 * jj + 3]);
                 }
         }
@@ -364,7 +577,7 @@ __global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t
     t /= tiles_n;
     const int mt = (int)(t % tiles_m);
     const int sp = (int)(t / tiles_m);
-    gemm_tile<WGM, WGN, TM, TN, TBK, NBUF, DMA, PARTIAL>(a, mt, nt, sp, k_per_split, sx, sw, [] {});
+    gemm_tile<WGM, WGN, TM, TN, TBK, NBUF, DMA, PARTIAL, false>(a, mt, nt, sp, k_per_split, sx, sw, [] {});
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -433,13 +646,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int32_t tiles
 }
 
 // One element of the split-K reduction: partials summed in split order, then the request-group
-// epilogue (columns below n_split) or the raw sum into Z.
+// epilogue (columns below n_split) or the raw sum into Z. COH: the partials were written during
+// this launch by other workgroups and are read with agent-coherent loads.
+template <bool COH = false>
 __device__ __forceinline__ void reduce_elem(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
                                             const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1,
                                             int64_t row, int32_t col) {
     const int64_t total = M * N, i = row * N + col;
     float s = 0.0f;
-    for (int sp = 0; sp < splits; ++sp) s += partial[(int64_t)sp * total + i];
+    for (int sp = 0; sp < splits; ++sp) s += COH ? load_coherent(partial + (int64_t)sp * total + i) : partial[(int64_t)sp * total + i];
     if (col < n_split) {
         float v = s + (bias0 ? bias0[col] : 0.0f);
         v = apply_act(act, v);
@@ -450,10 +665,65 @@ __device__ __forceinline__ void reduce_elem(const float *partial, int32_t splits
     }
 }
 
+// Four consecutive columns col .. col + 3 of the split-K reduction (N and n_split multiples of 4,
+// splits <= kMaxSplits): the partials of every split are loaded before the first add (a load per
+// split beyond `splits` rereads the last one and is not added), then summed in split order, which
+// gives the same bits as reduce_elem.
+constexpr int kMaxSplits = 16;
+template <bool COH = false>
+__device__ __forceinline__ void reduce_quad(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
+                                            const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1,
+                                            int64_t row, int32_t col) {
+    const int64_t total = M * N, i = row * N + col;
+    float4 p[kMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+        const float *q = partial + (int64_t)min(sp, splits - 1) * total + i;
+        if constexpr (COH) {
+            const uint64_t lo = __hip_atomic_load((const uint64_t *)q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t hi = __hip_atomic_load((const uint64_t *)q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            p[sp] = make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                                __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+        } else {
+            p[sp] = *(const float4 *)q;
+        }
+    }
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+        if (sp < splits) {
+            v[0] += p[sp].x; v[1] += p[sp].y; v[2] += p[sp].z; v[3] += p[sp].w;
+        }
+    if (col < n_split) {
+        if (bias0) {
+            const float4 b = *(const float4 *)(bias0 + col);
+            v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = apply_act(act, v[e]);
+        if (out0_f32) *(float4 *)((float *)out0 + row * n_split + col) = make_float4(v[0], v[1], v[2], v[3]);
+        else *(uint2 *)((uint16_t *)out0 + row * n_split + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    } else {
+        *(float4 *)(out1 + row * (N - n_split) + (col - n_split)) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+__device__ __forceinline__ bool reduce_quads_ok(int32_t splits, int32_t N, int32_t n_split) {
+    return splits >= 1 && splits <= kMaxSplits && (N & 3) == 0 && (n_split & 3) == 0;
+}
+
 __global__ void splitk_reduce_kernel(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
                                      const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1) {
     const int64_t total = M * N;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if (reduce_quads_ok(splits, N, n_split)) {
+        for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < total / 4; q += stride) {
+            const int64_t row = 4 * q / N;
+            reduce_quad(partial, splits, M, N, n_split, bias0, act, out0, out0_f32, out1, row, (int32_t)(4 * q - row * N));
+        }
+        return;
+    }
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += stride) {
         const int64_t row = i / N;
         reduce_elem(partial, splits, M, N, n_split, bias0, act, out0, out0_f32, out1, row, (int32_t)(i - row * N));
     }
@@ -465,11 +735,37 @@ __global__ void splitk_reduce_kernel(const float *partial, int32_t splits, int64
 // [16 .. 16 + Q) arrivals per request tile, [16 + Q .. 16 + 2Q) ready flags (Q request tiles).
 constexpr int kSyncHead = 16;
 
-__device__ __forceinline__ int32_t flag_load_acquire(const int32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+// A flag is read with a compare-exchange that never matches (flags hold 0 or 1): an atomic, so it
+// sees the device-wide value as the claim and arrival counters do. It is relaxed: the data a flag
+// guards is read with agent-coherent loads after the flag is seen, so no acquire fence (on this
+// part an L2 invalidate) is needed. A flag is set by a release fence (the writer's data reaches
+// memory) and an atomic exchange.
+__device__ __forceinline__ int32_t flag_poll(int32_t *p) {
+    int32_t v = 2;
+    __hip_atomic_compare_exchange_strong(p, &v, 2, __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
 }
-__device__ __forceinline__ void flag_store_release(int32_t *p, int32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void flag_release(int32_t *p, int32_t v) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Values every lane of a wave holds alike, moved to scalar registers so that the branches and loop
+// exits they decide are uniform. The control flow of the persistent loop below must be uniform:
+// with a loop exit that the compiler takes as divergent (a value read from LDS into a vector
+// register), it may run the loop for the other lanes while the one lane that claims items and
+// sets flags waits outside it, and the workgroup never ends.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+// lane 0 of the calling wave applies op, every lane gets its result (call with all lanes active)
+template <typename Op>
+__device__ __forceinline__ int32_t lane0(int lane, Op op) {
+    int32_t v = 0;
+    if (lane == 0) v = op();
+    return __builtin_amdgcn_readfirstlane(v);
 }
 
 template <bool DMA_R, bool DMA_C>
@@ -477,8 +773,9 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
     using G = GemmShape<kWGM, kWGN, kTM, kTN, BK>;
     IKBO_GEMM_LDS(G, 2);
     __shared__ int64_t s_item;
-    __shared__ int32_t s_last;
-    const int tid = threadIdx.x;
+    __shared__ int32_t s_flag;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int xcd = blockIdx.x % kNumXcd;
     const GemmArgs &rq = f.req, &cd = f.cand;
     const int32_t rtm = (int32_t)((rq.M + BM - 1) / BM), rtn = (rq.N + BN - 1) / BN;
@@ -490,77 +787,134 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
     const int64_t per_xcd = (cand_tiles + kNumXcd - 1) / kNumXcd;
     const int64_t c_beg = xcd * per_xcd, c_end = min(cand_tiles, c_beg + per_xcd);
     int32_t *arrive = f.sync + kSyncHead, *ready = f.sync + kSyncHead + req_tiles;
+    using CG = GemmShape<kWGM, kWGN, kTM, kTN, BK>;
 
-    for (;;) {
-        if (tid == 0) {
-            int64_t item = -1;
-            const int64_t r = atomicAdd(&f.sync[0], 1);
+    // wave 0 claims the next item (request items first, then this XCD's candidate tiles) and
+    // hands it to the workgroup through LDS
+    auto claim = [&]() -> int64_t {
+        if (wave == 0) {
+            int64_t it = -1;
+            const int32_t r = lane0(lane, [&] { return atomicAdd(&f.sync[0], 1); });
             if (r < req_items) {
-                item = r;
+                it = r;
             } else {
-                const int64_t c = c_beg + atomicAdd(&f.sync[1 + xcd], 1);
-                if (c < c_end) item = req_items + c;
+                const int64_t c = c_beg + lane0(lane, [&] { return atomicAdd(&f.sync[1 + xcd], 1); });
+                if (c < c_end) it = req_items + c;
             }
-            s_item = item;
+            if (lane == 0) s_item = it;
         }
         __syncthreads();
-        const int64_t item = s_item;
+        const int64_t it = uniform64(s_item);
         __syncthreads();
+        return it;
+    };
+    // request tiles wave 0 has seen ready (the first 64), so later tiles do not poll them again
+    uint64_t known = 0;
+    int64_t item = claim();
+    bool prefetched = false;
+    for (;;) {
         if (item < 0) break;
         if (item < req_items) {
             // request tile, one k split; splits of a tile are consecutive items
             const int64_t tile = item / splits;
             const int sp = (int)(item % splits);
             const int mt = (int)(tile / rtn), nt = (int)(tile % rtn);
-            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_R, true>(rq, mt, nt, sp, rkps, sx, sw, [] {});
-            __threadfence();                       // the partials are visible device-wide ...
+            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_R, true, false>(rq, mt, nt, sp, rkps, sx, sw, [] {});
+            // every wave's partial stores have reached the L2; one release (an L2 write-back) by
+            // wave 0 then puts them in memory before the arrival is counted
+            wait_vmcnt<0>();
             __syncthreads();
-            if (tid == 0) s_last = atomicAdd(&arrive[tile], 1) == splits - 1;    // ... before the arrival
+            if (wave == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                const int32_t a = lane0(lane, [&] { return atomicAdd(&arrive[tile], 1); });
+                if (lane == 0) s_flag = a == splits - 1;
+            }
             __syncthreads();
-            if (s_last) {
-                __threadfence();                   // the other splits' partials
+            if (__builtin_amdgcn_readfirstlane(s_flag)) {
+                // the last split of the tile: every other split's partials reached memory before its
+                // arrival was counted; they are read with coherent loads
                 const int64_t m0 = (int64_t)mt * BM;
                 const int n0 = nt * BN;
-                for (int i = tid; i < BM * BN; i += kGemmThreads) {
-                    const int64_t row = m0 + i / BN;
-                    const int col = n0 + i % BN;
-                    if (row < rq.M && col < rq.N)
-                        reduce_elem(rq.partial, splits, rq.M, rq.N, f.n_split, f.bias0, f.act, f.out0, f.out0_f32,
-                                    const_cast<float *>(cd.z), row, col);
+                float *z = const_cast<float *>(cd.z);
+                if (reduce_quads_ok(splits, rq.N, f.n_split)) {
+                    for (int i = tid; i < BM * BN / 4; i += kGemmThreads) {
+                        const int64_t row = m0 + i / (BN / 4);
+                        const int col = n0 + 4 * (i % (BN / 4));
+                        if (row < rq.M && col < rq.N)
+                            reduce_quad<true>(rq.partial, splits, rq.M, rq.N, f.n_split, f.bias0, f.act, f.out0,
+                                              f.out0_f32, z, row, col);
+                    }
+                } else {
+                    for (int i = tid; i < BM * BN; i += kGemmThreads) {
+                        const int64_t row = m0 + i / BN;
+                        const int col = n0 + i % BN;
+                        if (row < rq.M && col < rq.N)
+                            reduce_elem<true>(rq.partial, splits, rq.M, rq.N, f.n_split, f.bias0, f.act, f.out0,
+                                              f.out0_f32, z, row, col);
+                    }
                 }
-                __threadfence();
+                wait_vmcnt<0>();                   // Z and Y_r have reached the L2 ...
                 __syncthreads();
-                if (tid == 0) flag_store_release(&ready[tile], 1);
+                if (wave == 0 && lane == 0) flag_release(&ready[tile], 1);   // ... memory, then the flag
             }
+            item = claim();
+            prefetched = false;
         } else {
             const int64_t c = item - req_items;
             const int mt = (int)(c / ctn), nt = (int)(c % ctn);
-            // request tiles holding Z columns nt * BN .. nt * BN + BN - 1 (all request row blocks)
-            auto wait_z = [&] {
-                if (tid == 0) {
+            int64_t next = -1;
+            // After the main loop: wave 0 waits for the request tiles holding Z columns
+            // nt * BN .. nt * BN + BN - 1 (all request row blocks; bounded in time, and once any wait
+            // has run out, sync[9], every wait stops) and claims this XCD's next candidate tile,
+            // whose first k step then goes into LDS stage 0 (free once the main loop has ended)
+            // while this tile's epilogue runs (issued in the epilogue, after its first loads).
+            auto pre = [&] {
+                if (wave == 0) {
                     const int tn0 = (f.n_split + nt * BN) / BN;
                     const int tn1 = min(rtn - 1, (f.n_split + min(cd.N, nt * BN + BN) - 1) / BN);
-                    // once any wait has run out, later tiles do not wait again
-                    bool ok = flag_load_acquire(&f.sync[9]) == 0;
+                    const int64_t deadline = (int64_t)wall_clock64() + f.wait_ticks;
+                    bool ok = true;
                     for (int tm = 0; tm < rtm && ok; ++tm)
                         for (int tn = tn0; tn <= tn1 && ok; ++tn) {
-                            int64_t spins = 0;
-                            while (flag_load_acquire(&ready[(int64_t)tm * rtn + tn]) == 0) {
-                                if (++spins > f.spin_limit) {
+                            const int64_t ti = (int64_t)tm * rtn + tn;
+                            if (ti < 64 && ((known >> ti) & 1)) continue;
+                            if (lane0(lane, [&] { return flag_poll(&f.sync[9]); }) != 0) ok = false;
+                            while (ok && lane0(lane, [&] { return flag_poll(&ready[ti]); }) == 0) {
+                                if ((int64_t)wall_clock64() > deadline ||
+                                    lane0(lane, [&] { return flag_poll(&f.sync[9]); }) != 0) {
                                     ok = false;
-                                    atomicExch(&f.sync[9], 1);
-                                    break;
+                                    lane0(lane, [&] {
+                                        return __hip_atomic_exchange(&f.sync[9], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                    });
+                                } else {
+                                    __builtin_amdgcn_s_sleep(4);
                                 }
-                                __builtin_amdgcn_s_sleep(2);
                             }
+                            if (ok && ti < 64) known |= 1ull << ti;
                         }
-                    s_last = ok;
+                    const int64_t c2 = c_beg + lane0(lane, [&] { return atomicAdd(&f.sync[1 + xcd], 1); });
+                    if (lane == 0) {
+                        s_flag = ok;
+                        s_item = c2 < c_end ? req_items + c2 : -1;
+                    }
                 }
                 __syncthreads();
-                __threadfence();                   // acquire for every thread's Z reads
+                next = uniform64(s_item);
             };
-            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_C, false>(cd, mt, nt, 0, cd.K, sx, sw, wait_z);
-            if (!s_last) {
+            auto mid = [&] {
+                if constexpr (DMA_C) {
+                    if (next >= 0) {
+                        const int64_t c2 = next - req_items;
+                        const DmaTile t = dma_tile<CG, BK>(cd, (int)(c2 / ctn), (int)(c2 % ctn), 0, cd.K, wave, lane);
+                        dma_fetch<CG, BK>(cd, t, 0, sx[0], sw[0], wave);
+                    }
+                }
+            };
+            // the epilogue reads Z with plain loads when its lines hold one request tile each, else
+            // with coherent loads; no acquire fence, which would invalidate the XCD's L2 (and the
+            // weight and activation tiles the other workgroups there hold) per tile
+            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_C, false, true>(cd, mt, nt, 0, cd.K, sx, sw, pre, prefetched, mid);
+            if (!__builtin_amdgcn_readfirstlane(s_flag)) {
                 // the wait ran out: mark the tile's rows as invalid output
                 for (int i = tid; i < BM * BN; i += kGemmThreads) {
                     const int64_t row = (int64_t)mt * BM + i / BN;
@@ -571,9 +925,11 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
                     }
                 }
             }
-            __syncthreads();
+            item = next;
+            prefetched = DMA_C && next >= 0;
         }
     }
+    wait_vmcnt<0>();     // no copy may still be writing LDS when the workgroup ends
 }
 
 }  // namespace
@@ -635,6 +991,17 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
 #undef IKBO_GEMM
     }
     return hipGetLastError();
+}
+
+int64_t wall_clock_ticks(double seconds) {
+    static int khz = 0;
+    if (khz <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+            khz <= 0)
+            khz = 100000;     // 100 MHz
+    }
+    return (int64_t)(seconds * 1e3 * khz);
 }
 
 int64_t lcb_fused_sync_ints(int64_t M, int32_t N) {

@@ -96,9 +96,11 @@ struct LcbFusedArgs {
     void *out0;             // Y_r [R, n_split] or null when n_split == 0
     int32_t out0_f32;
     int32_t *sync;          // lcb_fused_sync_ints(...) int32, zeroed by launch_lcb_fused
-    int64_t spin_limit;     // bound on the flag wait (a wait that runs out sets sync[9] and poisons
-                            // the tile's output with NaN)
+    int64_t wait_ticks;     // bound on each flag wait, in ticks of the device's constant wall clock;
+                            // a wait that runs out sets sync[9] and poisons the tile's output with NaN
 };
+// ticks of the device's constant wall clock (wall_clock64) in the given number of seconds
+int64_t wall_clock_ticks(double seconds);
 // int32 words of synchronisation state for a request GEMM of M rows and N columns
 int64_t lcb_fused_sync_ints(int64_t M, int32_t N);
 // whether launch_lcb_fused supports these two GEMMs (bf16 with direct copies)

@@ -4,7 +4,9 @@ The oracle cannot evaluate whole workloads at these sizes, so each test compares
 candidates (first and last candidates of requests 0, 1, R/2 and R-1, plus seeded random ones)
 one by one against the fp64 oracle, and checks properties that hold at any size over every
 output: finiteness, and for attention the convexity bound min_j V <= O <= max_j V per request,
-head and channel."""
+head and channel. The persistent IKBO-LCB launch must equal the two-launch form bit for bit."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -80,11 +82,25 @@ def test_lcb_full_size():
     x_r, x_c = synth.glm_x(g, "x_r"), synth.glm_x(g, "x_c")
     w = synth.glm_weights(g, 0)
     wd = {k: up(v) for k, v in w.items()}
-    y_r, y_c = ikbo.ikbo_lcb_forward(up(x_r), up(x_c), wd["w_rr"], wd["w_cr"], wd["w_cc"], b_r=wd["b_r"],
-                                     b_c=wd["b_c"], cand_to_req=up(g.cand_to_req), sorted_index=True,
-                                     activation="gelu", out_dtype=torch.float32)
+    xr_d, xc_d, m_d = up(x_r), up(x_c), up(g.cand_to_req)
+
+    def call():
+        return ikbo.ikbo_lcb_forward(xr_d, xc_d, wd["w_rr"], wd["w_cr"], wd["w_cc"], b_r=wd["b_r"], b_c=wd["b_c"],
+                                     cand_to_req=m_d, sorted_index=True, activation="gelu", out_dtype=torch.float32)
+    y_r, y_c = call()
     torch.cuda.synchronize()
     assert torch.isfinite(y_c).all() and torch.isfinite(y_r).all()
+    # the persistent request/candidate launch gives the same bits at full size
+    note("full-size lcb, persistent launch")
+    os.environ["IKBO_LCB_FUSED"] = "1"
+    try:
+        y_r2, y_c2 = call()
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("IKBO_LCB_FUSED", None)
+    assert torch.equal(y_c2.view(torch.int32), y_c.view(torch.int32))
+    assert torch.equal(y_r2.view(torch.int32), y_r.view(torch.int32))
+    del y_r2, y_c2
     cands = sample_candidates(g.offsets, g.R)
     ly = dict(w, act="gelu")
     # compact oracle inputs: only the sampled candidates' rows

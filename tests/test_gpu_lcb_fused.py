@@ -3,7 +3,7 @@ candidate epilogue waiting on per-request-tile ready flags, ROCS Sec. 4.2.3) aga
 two-launch form and the fp64 oracle.
 
 The two forms run the same tile code with the same reduction order, so their outputs must agree
-bit for bit; the oracle bounds both. IKBO_LCB_TWO_LAUNCH=1 selects the two-launch form."""
+bit for bit; the oracle bounds both. IKBO_LCB_FUSED=1 selects the persistent launch."""
 import os
 
 import numpy as np
@@ -16,21 +16,19 @@ import synth
 from gpu_helpers import assert_parity, bf16_bits, down_f64, note
 from test_gpu_lcb import make_layer, make_x, run_lcb
 
-pytestmark = [pytest.mark.gpu,
-              pytest.mark.skip(reason="the persistent LCB launch is switched off: its first GPU run did not finish "
-                                      "(candidate tiles never observed the request tiles' ready flags); cause not "
-                                      "found yet")]
+pytestmark = pytest.mark.gpu
 
 COUNTS = np.array([1, 300, 0, 77, 513, 2, 40, 260, 5])
 
 
 def both_forms(fn):
-    os.environ["IKBO_LCB_TWO_LAUNCH"] = "1"
+    """(persistent launch result, two-launch result)"""
+    ref = fn()
+    os.environ["IKBO_LCB_FUSED"] = "1"
     try:
-        ref = fn()
+        return fn(), ref
     finally:
-        os.environ.pop("IKBO_LCB_TWO_LAUNCH", None)
-    return fn(), ref
+        os.environ.pop("IKBO_LCB_FUSED", None)
 
 
 def same_bits(a, b):
@@ -91,6 +89,10 @@ def test_fused_repeated_calls_reuse_the_workspace():
     x_r, x_c = make_x(23, R, C, 256, 256, "bf16")
     ly = make_layer(23, 256, 256, 256, 256, "bf16", "gelu")
     m = synth.cand_to_req_from_counts(COUNTS)
-    outs = [run_lcb(x_r, x_c, ly, m=m) for _ in range(3)]
+    os.environ["IKBO_LCB_FUSED"] = "1"
+    try:
+        outs = [run_lcb(x_r, x_c, ly, m=m) for _ in range(3)]
+    finally:
+        os.environ.pop("IKBO_LCB_FUSED", None)
     for yr, yc in outs[1:]:
         assert same_bits(yc, outs[0][1]) and same_bits(yr, outs[0][0])
