@@ -166,6 +166,44 @@ int ikbo_glm_mlp_forward(const void *x_req, int64_t num_req, const void *x_cand,
                          void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* ------------------------------------------------------------------------------------------
+ * K/V projection at the request batch size. Sec. 4.1 (the DCA decomposition after Eq. 14): a
+ * linear K/V projection commutes with the request-to-candidate broadcast, (S_m) W = (S W)_m, so
+ * K and V are projected once per request and the candidates of a request share the result.
+ *   k_out[i, :] = W_K s[i, :],   v_out[i, :] = W_V s[i, :]   for every sequence row i.
+ * s      [rows, d_in]: the request-side sequence rows of all requests stacked ([R * L, d_in] for
+ *        a uniform length L, [sum L_r, d_in] for variable lengths)                 (in_dtype)
+ * w_k, w_v  [d_out, d_in] (in_dtype): the pages' S W with W of shape [d_in, d_out], stored
+ *        transposed like the LCB weights (row n holds the weights of output n).
+ * k_out, v_out  [rows, d_out] (out_dtype). With d_out = num_heads * head_dim they are the
+ *        [rows, num_heads, head_dim] K / V that ikbo_dca_forward and ikbo_request_attention read.
+ * rows, d_in, d_out >= 0; d_in a multiple of 8 (bf16) / 4 (fp32), else IKBO_MISALIGNED.
+ * No workspace. Errors: IKBO_INVALID_ARGUMENT, IKBO_UNSUPPORTED, IKBO_MISALIGNED, IKBO_HIP_ERROR.
+ * ---------------------------------------------------------------------------------------- */
+int ikbo_kv_project(const void *s, int64_t rows, int32_t d_in, const void *w_k, const void *w_v,
+                    int32_t d_out, int32_t in_dtype, int32_t out_dtype, void *k_out, void *v_out,
+                    void *hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Request-side attention A^R of Deep Cross Attention (Sec. 3.2, Eq. 13, the request term): the
+ * queries of request r attend the K/V of request r, at the request batch size (no broadcast):
+ *   out[r, t, h, :] = sum_j softmax_j(scale * <q_req[r,t,h,:], k[r,j,h,:]>) * v[r, j, h, :].
+ * This is ikbo_dca_forward with one candidate per request (the identity map); with few query
+ * rows per request that call runs one-wave, 32-row work tiles.
+ * q_req  [num_req, q_len, num_heads, head_dim] (in_dtype)
+ * k, v, kv_cu_seqlens, kv_len, num_heads, head_dim, softmax_scale, in_dtype, out_dtype: as for
+ *        ikbo_dca_forward (the same head_dim and 2^31-byte limits).
+ * out    [num_req, q_len, num_heads, head_dim] (out_dtype); a request with L_r = 0 gets zeros.
+ * workspace >= ikbo_request_attention_workspace_size(num_req) bytes.
+ * Errors: as ikbo_dca_forward.
+ * ---------------------------------------------------------------------------------------- */
+size_t ikbo_request_attention_workspace_size(int64_t num_req);
+
+int ikbo_request_attention(const void *q_req, int64_t num_req, int32_t q_len, const void *k, const void *v,
+                           const int32_t *kv_cu_seqlens, int32_t kv_len, int32_t num_heads, int32_t head_dim,
+                           float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out,
+                           void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------------------------------------
  * Index check: counts, on the device, (a) candidates whose cand_to_req is outside
  * [0, num_req), (b) with IKBO_INDEX_SORTED, candidates whose map value is below the previous
  * candidate's, (c) when both arrays are given, candidates that are not inside

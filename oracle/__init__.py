@@ -14,6 +14,9 @@ then evaluates the definitions:
             per-group activation of Eq. 8, composed as in Sec. 3.1.5 Eq. 11. One layer is the
             IKBO-LCB linear form; two layers are the query MLP of Eq. 12.
 * ``gelu``  exact GELU x * Phi(x) via libm erf.
+* ``linear`` the request-side K/V projection, Sec. 4.1 (the DCA decomposition after Eq. 14):
+            y = x W^T in fp64 with a library matmul on exactly decoded inputs (numpy).
+* ``request_attention`` the request half A^R of Eq. 13: ``dca`` with one candidate per request.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py`` against library
 routines, closed forms, invariants and brute force on tiny inputs.
@@ -196,6 +199,32 @@ def glm(x_r: np.ndarray, x_c: np.ndarray, layers: Sequence[dict], *, m=None, off
     if return_violations:
         out["violations"] = viol.value
     return out
+
+
+def decode(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) or float32 -> exact float64 values."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
+    raise TypeError("oracle inputs are bf16 bit patterns (uint16) or float32, got %s" % a.dtype)
+
+
+def linear(x: np.ndarray, w: np.ndarray, *, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """y[i, n] = sum_k x[i, k] w[n, k] in fp64 (the projection S W of Sec. 4.1 with W stored as
+    [d_out, d_in]); x [rows, d_in], w [d_out, d_in]. Returns the rows `rows` (all when None)."""
+    xs = decode(x)
+    if rows is not None:
+        xs = xs[np.asarray(rows, dtype=np.int64)]
+    return xs @ decode(w).T
+
+
+def request_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, kv_cu=None, L: Optional[int] = None,
+                      scale: Optional[float] = None, nthreads: Optional[int] = None) -> np.ndarray:
+    """A^R: the queries of request r attend request r's K/V; q [R, Lq, H, d]."""
+    R = q.shape[0]
+    return dca(q, k, v, R, m=np.arange(R, dtype=np.int32), kv_cu=kv_cu, L=L, scale=scale, nthreads=nthreads)
 
 
 def index_violations(m, off, C: int, R: int, sorted_flag: bool = False) -> int:

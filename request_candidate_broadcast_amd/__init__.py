@@ -54,7 +54,8 @@ class GlmLayer(ctypes.Structure):
 EXPORTS = ["ikbo_version", "ikbo_status_string", "ikbo_last_error_message",
            "ikbo_dca_workspace_size", "ikbo_dca_forward",
            "ikbo_lcb_workspace_size", "ikbo_lcb_forward",
-           "ikbo_glm_mlp_workspace_size", "ikbo_glm_mlp_forward", "ikbo_check_index"]
+           "ikbo_glm_mlp_workspace_size", "ikbo_glm_mlp_forward", "ikbo_check_index",
+           "ikbo_kv_project", "ikbo_request_attention_workspace_size", "ikbo_request_attention"]
 
 _lib = None
 
@@ -93,6 +94,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          vp, vp, sz, vp]
     lib.ikbo_check_index.restype = ctypes.c_int
     lib.ikbo_check_index.argtypes = [vp, vp, i64, i64, u32, vp, vp]
+    lib.ikbo_kv_project.restype = ctypes.c_int
+    lib.ikbo_kv_project.argtypes = [vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.ikbo_request_attention_workspace_size.restype = sz
+    lib.ikbo_request_attention_workspace_size.argtypes = [i64]
+    lib.ikbo_request_attention.restype = ctypes.c_int
+    lib.ikbo_request_attention.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, i32, f32, i32, i32, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -198,6 +205,64 @@ def ikbo_dca_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, num_r
                               0 if ws is None else ws.numel(), _stream(stream))
     _check(st)
     return out
+
+
+# ------------------------------------------------------------------------------------------------
+def ikbo_request_attention_workspace_size(num_req: int) -> int:
+    return int(load_library().ikbo_request_attention_workspace_size(num_req))
+
+
+def ikbo_request_attention(q_req: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                           kv_cu_seqlens: Optional[torch.Tensor] = None, kv_len: Optional[int] = None,
+                           softmax_scale: float = 0.0, out_dtype=None, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Request-side attention A^R. q_req [R, Lq, H, d]; k, v [R, L, H, d] or varlen [sum L_r, H, d] with
+    kv_cu_seqlens [R+1]. Returns out [R, Lq, H, d] in out_dtype (default: q_req's dtype)."""
+    lib = load_library()
+    for n, t in (("q_req", q_req), ("k", k), ("v", v)):
+        _need_contig(n, t)
+    R, Lq, H, d = q_req.shape
+    kv_cu_seqlens = _index(kv_cu_seqlens, "kv_cu_seqlens")
+    if kv_len is None:
+        kv_len = k.shape[1] if (kv_cu_seqlens is None and k.dim() == 4) else 0
+    in_code = _dt(q_req)
+    out_code = in_code if out_dtype is None else _dt(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty((R, Lq, H, d), dtype=_torch_dtype(out_code), device=q_req.device)
+    else:
+        out_code = _dt(out)
+    ws = _workspace(ikbo_request_attention_workspace_size(R), q_req.device, workspace)
+    st = lib.ikbo_request_attention(_ptr(q_req), R, Lq, _ptr(k), _ptr(v), _ptr(kv_cu_seqlens), kv_len, H, d,
+                                    float(softmax_scale), in_code, out_code, _ptr(out), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream))
+    _check(st)
+    return out
+
+
+def ikbo_kv_project(s: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, *, out_dtype=None,
+                    k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None, stream=None):
+    """K/V projection at the request batch. s [rows, d_in]; w_k, w_v [d_out, d_in].
+    Returns (k_out, v_out), each [rows, d_out] in out_dtype (default: s's dtype)."""
+    lib = load_library()
+    for n, t in (("s", s), ("w_k", w_k), ("w_v", w_v)):
+        _need_contig(n, t)
+    rows, d_in = s.shape
+    d_out = w_k.shape[0]
+    if tuple(w_k.shape) != (d_out, d_in) or tuple(w_v.shape) != (d_out, d_in):
+        raise ValueError("w_k and w_v must be [d_out, d_in]")
+    in_code = _dt(s)
+    out_code = in_code if out_dtype is None else _dt(torch.empty(0, dtype=out_dtype))
+    if k_out is None:
+        k_out = torch.empty((rows, d_out), dtype=_torch_dtype(out_code), device=s.device)
+    if v_out is None:
+        v_out = torch.empty((rows, d_out), dtype=_torch_dtype(out_code), device=s.device)
+    if k_out.dtype != v_out.dtype:
+        raise TypeError("k_out and v_out must share a dtype")
+    out_code = _dt(k_out)
+    st = lib.ikbo_kv_project(_ptr(s), rows, d_in, _ptr(w_k), _ptr(w_v), d_out, in_code, out_code, _ptr(k_out),
+                             _ptr(v_out), _stream(stream))
+    _check(st)
+    return k_out, v_out
 
 
 # ------------------------------------------------------------------------------------------------

@@ -278,12 +278,12 @@ size_t ikbo_dca_workspace_size(int64_t num_cand, int64_t num_req) {
     return dca_ws(num_cand, num_req, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
-int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len, const void *k, const void *v, int64_t num_req,
-                     const int32_t *kv_cu_seqlens, int32_t kv_len, const int32_t *cand_to_req,
-                     const int32_t *req_cand_offsets, uint32_t index_flags, int32_t num_heads, int32_t head_dim,
-                     float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out, void *workspace,
-                     size_t workspace_bytes, void *hip_stream) {
-    const int64_t C = num_cand, R = num_req;
+// Argument checks of ikbo_dca_forward (nothing enqueued)
+static int dca_validate(const void *q, int64_t C, int32_t q_len, const void *k, const void *v, int64_t R,
+                        const int32_t *kv_cu_seqlens, int32_t kv_len, const int32_t *cand_to_req,
+                        const int32_t *req_cand_offsets, uint32_t index_flags, int32_t num_heads, int32_t head_dim,
+                        int32_t in_dtype, int32_t out_dtype, const void *out, const void *workspace,
+                        size_t workspace_bytes) {
     if (C < 0 || R < 0 || q_len <= 0 || num_heads <= 0 || head_dim <= 0 || kv_len < 0)
         return fail(IKBO_INVALID_ARGUMENT, "bad sizes (num_cand %lld num_req %lld q_len %d heads %d head_dim %d kv_len %d)",
                     (long long)C, (long long)R, q_len, num_heads, head_dim, kv_len);
@@ -306,16 +306,25 @@ int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len, const void 
     const size_t need = ikbo_dca_workspace_size(C, R);
     if (workspace_bytes < need || (!workspace && need > 0))
         return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    return IKBO_OK;
+}
+
+// The DCA launches of ikbo_dca_forward, arguments already validated
+static int dca_run(const void *q, int64_t C, int32_t q_len, const void *k, const void *v, int64_t R,
+                   const int32_t *kv_cu_seqlens, int32_t kv_len, const int32_t *cand_to_req,
+                   const int32_t *req_cand_offsets, int32_t num_heads, int32_t head_dim, float softmax_scale,
+                   int32_t in_dtype, int32_t out_dtype, void *out, void *workspace, hipStream_t s) {
     if (C == 0) return ok();
-    hipStream_t s = (hipStream_t)hip_stream;
     const int in_f32 = in_dtype == IKBO_F32;
     const int64_t row_elems = (int64_t)q_len * num_heads * head_dim;
     const int ob = (int)esize(out_dtype);
+    // few stacked query rows per request (at most 32 on average): one-wave, 32-row work tiles
+    const int small = !in_f32 && C * (int64_t)q_len <= 32 * R;
 
     Carver cv(workspace);
     int32_t *counts, *off, *tiles, *perm;
     dca_ws(C, R, &cv, &counts, &off, &tiles, &perm);
-    const int32_t bm = ikbo::dca_block_m(head_dim, in_f32);
+    const int32_t bm = ikbo::dca_block_m(head_dim, in_f32, small);
     const int32_t *perm_used = nullptr;
     if (req_cand_offsets) {
         IKBO_HIP(ikbo::launch_scan_tiles(nullptr, req_cand_offsets, R, C, q_len, num_heads, bm, off, nullptr, tiles, s));
@@ -348,7 +357,85 @@ int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len, const void 
     a.scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
     a.in_f32 = in_f32;
     a.out_f32 = out_dtype == IKBO_F32;
+    a.small = small;
     IKBO_HIP(ikbo::launch_dca(a, s));
+    return ok();
+}
+
+int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len, const void *k, const void *v, int64_t num_req,
+                     const int32_t *kv_cu_seqlens, int32_t kv_len, const int32_t *cand_to_req,
+                     const int32_t *req_cand_offsets, uint32_t index_flags, int32_t num_heads, int32_t head_dim,
+                     float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out, void *workspace,
+                     size_t workspace_bytes, void *hip_stream) {
+    const int rc = dca_validate(q, num_cand, q_len, k, v, num_req, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets,
+                                index_flags, num_heads, head_dim, in_dtype, out_dtype, out, workspace, workspace_bytes);
+    if (rc) return rc;
+    return dca_run(q, num_cand, q_len, k, v, num_req, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets, num_heads,
+                   head_dim, softmax_scale, in_dtype, out_dtype, out, workspace, (hipStream_t)hip_stream);
+}
+
+// ---- request-side attention ---------------------------------------------------------------------
+size_t ikbo_request_attention_workspace_size(int64_t num_req) {
+    if (num_req < 0) return 0;
+    return align256(sizeof(int32_t) * (size_t)(num_req + 1)) + ikbo_dca_workspace_size(num_req, num_req);
+}
+
+int ikbo_request_attention(const void *q_req, int64_t num_req, int32_t q_len, const void *k, const void *v,
+                           const int32_t *kv_cu_seqlens, int32_t kv_len, int32_t num_heads, int32_t head_dim,
+                           float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out, void *workspace,
+                           size_t workspace_bytes, void *hip_stream) {
+    const int64_t R = num_req;
+    if (R < 0) return fail(IKBO_INVALID_ARGUMENT, "negative num_req");
+    const size_t need = ikbo_request_attention_workspace_size(R);
+    if (workspace_bytes < need || !workspace)
+        return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    // the identity map as offsets (request r is candidate r), then the DCA over it
+    Carver cv(workspace);
+    int32_t *ident = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(R + 1));
+    void *rest = (char *)workspace + cv.used;
+    const size_t rest_bytes = workspace_bytes - cv.used;
+    const int rc = dca_validate(q_req, R, q_len, k, v, R, kv_cu_seqlens, kv_len, nullptr, ident, IKBO_INDEX_SORTED,
+                                num_heads, head_dim, in_dtype, out_dtype, out, rest, rest_bytes);
+    if (rc) return rc;
+    if (R == 0) return ok();
+    hipStream_t s = (hipStream_t)hip_stream;
+    IKBO_HIP(ikbo::launch_iota_i32(ident, R + 1, s));
+    return dca_run(q_req, R, q_len, k, v, R, kv_cu_seqlens, kv_len, nullptr, ident, num_heads, head_dim, softmax_scale,
+                   in_dtype, out_dtype, out, rest, s);
+}
+
+// ---- K/V projection -----------------------------------------------------------------------------
+int ikbo_kv_project(const void *s_rows, int64_t rows, int32_t d_in, const void *w_k, const void *w_v, int32_t d_out,
+                    int32_t in_dtype, int32_t out_dtype, void *k_out, void *v_out, void *hip_stream) {
+    if (rows < 0 || d_in < 0 || d_out < 0)
+        return fail(IKBO_INVALID_ARGUMENT, "bad sizes (rows %lld d_in %d d_out %d)", (long long)rows, d_in, d_out);
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(IKBO_UNSUPPORTED, "dtype in %d out %d", in_dtype, out_dtype);
+    if (rows == 0 || d_out == 0) return ok();
+    if (!s_rows || !w_k || !w_v || !k_out || !v_out) return fail(IKBO_INVALID_ARGUMENT, "a tensor pointer is NULL");
+    const void *ptrs[] = {s_rows, w_k, w_v, k_out, v_out};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    const int in_f32 = in_dtype == IKBO_F32;
+    if (d_in % (in_f32 ? 4 : 8)) return fail(IKBO_MISALIGNED, "d_in must keep 16-byte rows (got %d)", d_in);
+    hipStream_t s = (hipStream_t)hip_stream;
+    // one GEMM per projection: out = s W^T, no bias, no activation, no gather
+    for (int which = 0; which < 2; ++which) {
+        ikbo::GemmArgs g = {};
+        g.x = s_rows;
+        g.M = rows;
+        g.K = d_in;
+        g.ldx = d_in;
+        g.w0 = which ? w_v : w_k;
+        g.w1 = g.w0;
+        g.n0 = d_out;
+        g.N = d_out;
+        g.in_f32 = in_f32;
+        g.out = which ? v_out : k_out;
+        g.ldo = d_out;
+        g.out_f32 = out_dtype == IKBO_F32;
+        IKBO_HIP(ikbo::launch_gemm(g, s));
+    }
     return ok();
 }
 

@@ -374,13 +374,18 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
     // The copies of tile it + 1 go out one per k16 step of tile it's scores, so the eight waves
     // do not queue all their copies at once right after the barrier; the copy unit is fed while
     // the MFMAs run. Each barrier waits for the whole next tile.
-    // COPYAT 0: all copies in the k16 steps of the scores; 1: in the 32-dim steps of PV; 2: split
+    // COPYAT 0: all copies in the k16 steps of the scores (kCPS per step: one with eight waves,
+    // more when fewer waves share a tile's copies); 1: in the 32-dim steps of PV; 2: split
     constexpr int kInS = COPYAT == 0 ? kCopiesPerTile : COPYAT == 1 ? 0 : (kCopiesPerTile + 1) / 2;
     constexpr int kInPv = kCopiesPerTile - kInS;
-    static_assert(kInS <= KS && (kInPv + DB - 1) / DB <= 2, "copy spreading");
+    constexpr int kCPS = (kInS + KS - 1) / KS;
+    static_assert((COPYAT == 0 || kInS <= KS) && (kInPv + DB - 1) / DB <= 2, "copy spreading");
     auto step = [&](int it, auto S, auto mask) __attribute__((always_inline)) {
         auto copies_s = [&](auto ks) __attribute__((always_inline)) {
-            if constexpr (ks < kInS) copy(ks, (it + 1) * BN, IC<(S + 1) % NBUF>{});
+            static_for<kCPS>([&](auto u) __attribute__((always_inline)) {
+                constexpr int c = decltype(ks)::value * kCPS + decltype(u)::value;
+                if constexpr (c < kInS) copy(c, (it + 1) * BN, IC<(S + 1) % NBUF>{});
+            });
         };
         auto copies_pv = [&](auto db) __attribute__((always_inline)) {
             if constexpr (db < kInPv) copy(kInS + db, (it + 1) * BN, IC<(S + 1) % NBUF>{});
@@ -457,11 +462,13 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
         }
 }
 
-// The configuration the library launches, per head dim.
-template <int D>
+// The configurations the library launches, per head dim: 8 waves x 32 query rows, 64-key tiles,
+// two LDS stages, K reads two k16 steps ahead; and, for requests with few stacked query rows (the
+// request-side attention has q_len rows per request), one wave of 32 rows, so a work tile is not
+// mostly empty rows (each row's arithmetic is the same in both, so are the results).
+template <int D, bool SMALL = false>
 struct DcaBf16Config {
-    // 8 waves x 32 query rows, 64-key tiles, two LDS stages, K reads two k16 steps ahead
-    static constexpr int NW = 8, NKB = 2, NBUF = 2, KPD = 1, VPD = 1, COPYAT = 0;
+    static constexpr int NW = SMALL ? 1 : 8, NKB = 2, NBUF = 2, KPD = 1, VPD = 1, COPYAT = 0;
     static constexpr int BM = NW * 32;
 };
 
@@ -554,8 +561,9 @@ __global__ __launch_bounds__(256) void dca_f32_kernel(DcaArgs a) {
 
 }  // namespace
 
-int32_t dca_block_m(int32_t D, int in_f32) {
+int32_t dca_block_m(int32_t D, int in_f32, int small) {
     if (in_f32) return kF32Rows;
+    if (small) return D == 128 ? DcaBf16Config<128, true>::BM : DcaBf16Config<64, true>::BM;
     return D == 128 ? DcaBf16Config<128>::BM : DcaBf16Config<64>::BM;
 }
 
@@ -565,14 +573,21 @@ hipError_t launch_dca(const DcaArgs &a, hipStream_t s) {
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (a.in_f32) {
         hipLaunchKernelGGL(dca_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
-    } else if (a.D == 128) {
-        using C = DcaBf16Config<128>;
-        hipLaunchKernelGGL((dca_bf16_kernel<128, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD, C::COPYAT>), dim3((unsigned)grid),
-                           dim3(C::NW * 64), 0, s, a);
-    } else if (a.D == 64) {
-        using C = DcaBf16Config<64>;
-        hipLaunchKernelGGL((dca_bf16_kernel<64, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD, C::COPYAT>), dim3((unsigned)grid),
-                           dim3(C::NW * 64), 0, s, a);
+    } else if (a.D == 128 || a.D == 64) {
+#define IKBO_DCA_LAUNCH(DD, SM)                                                                                         \
+    do {                                                                                                               \
+        using C = DcaBf16Config<DD, SM>;                                                                               \
+        hipLaunchKernelGGL((dca_bf16_kernel<DD, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD, C::COPYAT>), dim3((unsigned)grid), \
+                           dim3(C::NW * 64), 0, s, a);                                                                 \
+    } while (0)
+        if (a.D == 128) {
+            if (a.small) IKBO_DCA_LAUNCH(128, true);
+            else IKBO_DCA_LAUNCH(128, false);
+        } else {
+            if (a.small) IKBO_DCA_LAUNCH(64, true);
+            else IKBO_DCA_LAUNCH(64, false);
+        }
+#undef IKBO_DCA_LAUNCH
     } else {
         return hipErrorInvalidValue;
     }

@@ -16,6 +16,11 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+__global__ void iota_i32_kernel(int32_t *p, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = (int32_t)i;
+}
+
 __global__ void histogram_kernel(const int32_t *m, int64_t C, int64_t R, int32_t *counts) {
     for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < C; c += (int64_t)gridDim.x * blockDim.x) {
         const int32_t r = m[c];
@@ -161,6 +166,12 @@ unsigned grid_for(int64_t n, int threads) {
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, p, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_iota_i32(int32_t *p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(iota_i32_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

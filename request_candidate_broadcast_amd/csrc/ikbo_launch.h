@@ -10,6 +10,8 @@ namespace ikbo {
 // ---- index prologue (ikbo_index.hip) ----------------------------------------------------------
 // Fill n int32 with a value (a kernel, not hipMemsetAsync, so it is safe under graph capture).
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t s);
+// p[i] = i for i < n
+hipError_t launch_iota_i32(int32_t *p, int64_t n, hipStream_t s);
 // counts[r] += 1 for every candidate with 0 <= m[c] < R.
 hipError_t launch_histogram(const int32_t *m, int64_t C, int64_t R, int32_t *counts, hipStream_t s);
 // From counts (counts != null) or from offsets: writes off_out[0..R] (exclusive scan of counts, or a
@@ -43,9 +45,10 @@ struct DcaArgs {
     int64_t grid_tiles;         // upper bound on tile_start[R], sizes the grid
     float scale;
     int32_t in_f32, out_f32;
+    int32_t small;              // bf16: the one-wave configuration (32 rows per work tile)
 };
 // Rows of stacked candidate queries covered by one DCA work tile, per path.
-int32_t dca_block_m(int32_t D, int in_f32);
+int32_t dca_block_m(int32_t D, int in_f32, int small);
 hipError_t launch_dca(const DcaArgs &a, hipStream_t s);
 
 // ---- GEMMs for IKBO-LCB (ikbo_gemm.hip) ------------------------------------------------------

@@ -154,3 +154,44 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load_library(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+def kvp(lib, **kw):
+    a = dict(s=FAKE, rows=1024, d_in=256, wk=FAKE, wv=FAKE, d_out=128, ind=1, outd=1, k=FAKE, v=FAKE, stream=None)
+    a.update(kw)
+    return lib.ikbo_kv_project(a["s"], a["rows"], a["d_in"], a["wk"], a["wv"], a["d_out"], a["ind"], a["outd"],
+                               a["k"], a["v"], a["stream"])
+
+
+def test_kv_project_argument_errors(lib):
+    assert kvp(lib, rows=-1) == ikbo.IKBO_INVALID_ARGUMENT
+    assert kvp(lib, ind=7) == ikbo.IKBO_UNSUPPORTED
+    assert kvp(lib, wv=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert kvp(lib, k=MIS) == ikbo.IKBO_MISALIGNED
+    assert kvp(lib, d_in=100) == ikbo.IKBO_MISALIGNED          # bf16 rows need d_in % 8 == 0
+    assert b"d_in" in lib.ikbo_last_error_message()
+    # nothing to compute: OK without touching the GPU
+    assert kvp(lib, rows=0) == ikbo.IKBO_OK
+    assert kvp(lib, d_out=0) == ikbo.IKBO_OK
+
+
+def rattn(lib, **kw):
+    a = dict(q=FAKE, R=8, Lq=4, k=FAKE, v=FAKE, cu=None, L=64, H=2, d=128, scale=0.0, ind=1, outd=0, out=FAKE,
+             ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.ikbo_request_attention(a["q"], a["R"], a["Lq"], a["k"], a["v"], a["cu"], a["L"], a["H"], a["d"],
+                                      a["scale"], a["ind"], a["outd"], a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_request_attention_argument_errors(lib):
+    need = lib.ikbo_request_attention_workspace_size(8)
+    assert need >= 4 * 9 + lib.ikbo_dca_workspace_size(8, 8)
+    assert lib.ikbo_request_attention_workspace_size(-1) == 0
+    assert rattn(lib, R=-1) == ikbo.IKBO_INVALID_ARGUMENT
+    assert rattn(lib, wsb=need - 1) == ikbo.IKBO_WORKSPACE_TOO_SMALL
+    assert rattn(lib, d=96) == ikbo.IKBO_UNSUPPORTED
+    assert rattn(lib, L=1 << 20, H=8) == ikbo.IKBO_UNSUPPORTED
+    assert b"2^31" in lib.ikbo_last_error_message()
+    assert rattn(lib, q=MIS) == ikbo.IKBO_MISALIGNED
+    assert rattn(lib, Lq=0) == ikbo.IKBO_INVALID_ARGUMENT
+    assert rattn(lib, R=0) == ikbo.IKBO_OK
