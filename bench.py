@@ -33,7 +33,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="block", choices=["block", "dca_fixed", "dca_ragged", "lcb"])
+    p.add_argument("--workload", default="block", choices=["block", "layer", "dca_fixed", "dca_ragged", "lcb"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=0, help="candidates in the oracle sample (0 = default)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -95,7 +95,7 @@ def main():
     flops = {}
     algo_bytes = {}
     with torch.cuda.stream(stream):
-        if args.workload in ("block",):
+        if args.workload in ("block", "layer"):
             g, s = synth.block_specs()
             x_r = up(synth.glm_x(g, "x_r"))
             x_c = up(synth.glm_x(g, "x_c"))
@@ -137,6 +137,43 @@ def main():
                       "requests": s.R, "candidates": s.C, "cand_per_request": int(s.counts[0]),
                       "mlp": "[4096|2048] -> 2048 (GELU) -> 4096", "kv_len": s.L, "heads": s.H, "head_dim": s.d,
                       "q_tokens": s.Lq}
+            if args.workload == "layer":
+                # the whole DCA layer: K/V of both halves projected from the request sequence rows
+                # S once per request, A^C = IKBO-DCA(q_c, K^C, V^C), A^R = Attn(q_r, K^R, V^R)
+                del k, v
+                seq = up(synth.seq_rows(s))
+                wk = {n: up(synth.kv_weight(s, n)) for n in ("w_kc", "w_vc", "w_kr", "w_vr")}
+                hd, rows = s.H * s.d, s.kv_rows
+                kc = torch.empty((rows, hd), dtype=torch.bfloat16, device=dev)
+                vc, kr, vr = torch.empty_like(kc), torch.empty_like(kc), torch.empty_like(kc)
+                q_r = y_req.view(s.R, s.Lq, s.H, s.d)
+                out_r = torch.empty((s.R, s.Lq, s.H, s.d), dtype=torch.bfloat16, device=dev)
+                ws_ra = torch.empty(ikbo.ikbo_request_attention_workspace_size(s.R), dtype=torch.uint8, device=dev)
+                d_in = synth.seq_width(s)
+                flops["kv_proj_c"] = flops["kv_proj_r"] = 2 * 2.0 * rows * d_in * hd
+                flops["attn_r"] = 4.0 * s.R * s.Lq * s.H * s.d * s.L
+                algo_bytes["kv_proj_c"] = algo_bytes["kv_proj_r"] = 2 * (rows * d_in + 2 * rows * hd + 2 * hd * d_in)
+                algo_bytes["attn_r"] = 2 * (2 * s.R * s.Lq * hd + 2 * rows * hd)
+
+                def step(ev):
+                    ev[0].record(stream)
+                    ikbo.ikbo_glm_mlp_forward(x_r, x_c, layers, cand_to_req=m, sorted_index=True, y_req=y_req,
+                                              y_cand=y_cand, workspace=ws_mlp, stream=stream)
+                    ev[1].record(stream)
+                    ikbo.ikbo_kv_project(seq, wk["w_kc"], wk["w_vc"], k_out=kc, v_out=vc, stream=stream)
+                    ev[2].record(stream)
+                    ikbo.ikbo_dca_forward(q, kc.view(s.R, s.L, s.H, s.d), vc.view(s.R, s.L, s.H, s.d),
+                                          req_cand_offsets=off, out=out, workspace=ws_dca, stream=stream)
+                    ev[3].record(stream)
+                    ikbo.ikbo_kv_project(seq, wk["w_kr"], wk["w_vr"], k_out=kr, v_out=vr, stream=stream)
+                    ev[4].record(stream)
+                    ikbo.ikbo_request_attention(q_r, kr.view(s.R, s.L, s.H, s.d), vr.view(s.R, s.L, s.H, s.d),
+                                                out=out_r, workspace=ws_ra, stream=stream)
+                    ev[5].record(stream)
+
+                names = [("mlp", 0, 1), ("kv_proj_c", 1, 2), ("dca", 2, 3), ("kv_proj_r", 3, 4), ("attn_r", 4, 5)]
+                config = dict(config, workload="ROCS DCA layer: GLM-MLP -> K/V projections of S (once per request) "
+                              "-> A^C (IKBO-DCA) + A^R (request-side attention)", seq_width=d_in)
         elif args.workload in ("dca_fixed", "dca_ragged"):
             s = synth.dca_spec(args.workload)
             q = up(synth.dca_q(s))
@@ -283,7 +320,7 @@ def cpu_baseline(args, np):
     import synth
     nthreads = max(1, min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
-    if args.workload == "block":
+    if args.workload in ("block", "layer"):
         g, s = synth.block_specs()
         n_per = args.cpu_sample // 4 if args.cpu_sample else 96
         reqs = [0, 1, g.R // 2, g.R - 1]
@@ -299,11 +336,26 @@ def cpu_baseline(args, np):
         n = len(m_sub)
         log("cpu baseline: oracle on %d candidates with %d threads" % (n, nthreads))
         t0 = time.perf_counter()
-        qo = oracle.glm(x_r, x_c, layers, m=m_sub, nthreads=nthreads)["y_c"]
+        res = oracle.glm(x_r, x_c, layers, m=m_sub, want_request=args.workload == "layer", nthreads=nthreads)
+        qo = res["y_c"]
         oracle.dca(qo.reshape(n, s.Lq, s.H, s.d), k, v, len(reqs), m=m_kv, nthreads=nthreads)
         secs = time.perf_counter() - t0
         work = (g.flops() + s.flops()) / g.C * n
         sample = "%d candidates (the first %d of requests %s): GLM-MLP then DCA, chained in fp64" % (n, n_per, reqs)
+        if args.workload == "layer":
+            # plus, for request 0: its four K/V projections and its request-side attention
+            r0, hd, d_in = reqs[0], s.H * s.d, synth.seq_width(s)
+            rows_r = synth.seq_rows(s, r0 * s.L, s.L)
+            wts = [synth.kv_weight(s, nm) for nm in ("w_kc", "w_vc", "w_kr", "w_vr")]
+            t1 = time.perf_counter()
+            proj = [oracle.linear(rows_r, w) for w in wts]
+            kr = proj[2].astype(np.float32).reshape(1, s.L, s.H, s.d)
+            vr = proj[3].astype(np.float32).reshape(1, s.L, s.H, s.d)
+            q_r = res["y_r"][r0].astype(np.float32).reshape(1, s.Lq, s.H, s.d)
+            oracle.request_attention(q_r, kr, vr, nthreads=nthreads)
+            secs += time.perf_counter() - t1
+            work += 4 * 2.0 * s.L * d_in * hd + 4.0 * s.Lq * s.H * s.d * s.L
+            sample += "; plus the four K/V projections of request %d's %d sequence rows and its A^R" % (r0, s.L)
     elif args.workload in ("dca_fixed", "dca_ragged"):
         s = synth.dca_spec(args.workload)
         reqs = [0, 1, s.R // 2, s.R - 1]

@@ -38,6 +38,7 @@ _NP = {"f64": np.float64, "f32": np.float32, "bf16": np.uint16, "unif": np.float
 TAGS = {
     "counts": 1, "kv_len": 2, "q": 3, "k": 4, "v": 5,
     "x_r": 6, "x_c": 7, "w_rr": 8, "w_cr": 9, "w_cc": 10, "b_r": 11, "b_c": 12,
+    "s": 13, "w_kc": 14, "w_vc": 15, "w_kr": 16, "w_vr": 17,
 }
 
 
@@ -330,6 +331,28 @@ def glm_weights(spec: GlmSpec, layer: int) -> dict:
         "b_r": draw(s, tag("b_r"), ly.n_req, "f32", sr),
         "b_c": draw(s, tag("b_c"), ly.n_cand, "f32", sc),
     }
+
+
+# Width of the request-side sequence rows S that the K/V projections read. The pages give none;
+# taken as num_heads * head_dim (a square projection).
+def seq_width(spec: "DcaSpec") -> int:
+    return spec.H * spec.d
+
+
+def seq_rows(spec: "DcaSpec", row_start: int = 0, row_count: Optional[int] = None) -> np.ndarray:
+    """Rows [row_start, row_start + row_count) of the stacked sequence rows S [kv_rows, seq_width],
+    N(0, 1) in the spec's dtype."""
+    n = spec.kv_rows - row_start if row_count is None else row_count
+    w = seq_width(spec)
+    return draw(spec.seed, TAGS["s"], n * w, spec.dtype, 1.0, start=row_start * w).reshape(n, w)
+
+
+def kv_weight(spec: "DcaSpec", name: str) -> np.ndarray:
+    """A K/V projection weight [H*d, seq_width] ("w_kc", "w_vc": the candidate half's W^C_K, W^C_V;
+    "w_kr", "w_vr": the request half's), N(0, 1/seq_width)."""
+    w = seq_width(spec)
+    n = spec.H * spec.d
+    return draw(spec.seed, TAGS[name], n * w, spec.dtype, 1.0 / np.sqrt(w)).reshape(n, w)
 
 
 def block_specs():
