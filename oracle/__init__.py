@@ -17,6 +17,9 @@ then evaluates the definitions:
 * ``linear`` the request-side K/V projection, Sec. 4.1 (the DCA decomposition after Eq. 14):
             y = x W^T in fp64 with a library matmul on exactly decoded inputs (numpy).
 * ``request_attention`` the request half A^R of Eq. 13: ``dca`` with one candidate per request.
+* ``fm``    the GLM factorization machine, Sec. 3.1.4 Eq. 9-10 (two groups): request outputs
+            X^R (X^R)^T, candidate outputs [X^C (X^R_m)^T, X^C (X^C)^T], in fp64 with the request
+            rows expanded per candidate.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py`` against library
 routines, closed forms, invariants and brute force on tiny inputs.
@@ -225,6 +228,30 @@ def request_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, kv_cu=None
     """A^R: the queries of request r attend request r's K/V; q [R, Lq, H, d]."""
     R = q.shape[0]
     return dca(q, k, v, R, m=np.arange(R, dtype=np.int32), kv_cu=kv_cu, L=L, scale=scale, nthreads=nthreads)
+
+
+def fm(x_r: np.ndarray, x_c: np.ndarray, *, m=None, off=None, cands: Optional[Sequence[int]] = None,
+       want_request: bool = False):
+    """GLM factorization machine, two groups (Eq. 10). x_r [R, n_r, d], x_c [C, n_c, d] (bf16 bits or
+    fp32). Returns {"y_c": [n, n_c, n_r + n_c]} for the candidates `cands` (all when None) and, with
+    want_request, "y_r": [R, n_r, n_r]. A candidate whose request is out of range (or not covered by
+    the offsets) gets zeros."""
+    xr, xc = decode(x_r), decode(x_c)
+    R, n_r, _ = xr.shape
+    C, n_c, _ = xc.shape
+    ids = np.arange(C) if cands is None else np.asarray(cands, dtype=np.int64)
+    y_c = np.zeros((len(ids), n_c, n_r + n_c), dtype=np.float64)
+    mm, oo = _i32(m), _i32(off)
+    for o, c in enumerate(ids):
+        r = int(_get().oracle_request_of(_ptr(mm), _ptr(oo), R, int(c)))
+        if r < 0:
+            continue
+        y_c[o, :, :n_r] = xc[c] @ xr[r].T          # request-candidate interactions (the broadcast term)
+        y_c[o, :, n_r:] = xc[c] @ xc[c].T          # candidate-candidate interactions
+    out = {"y_c": y_c}
+    if want_request:
+        out["y_r"] = np.stack([xr[r] @ xr[r].T for r in range(R)]) if R else np.zeros((0, n_r, n_r))
+    return out
 
 
 def index_violations(m, off, C: int, R: int, sorted_flag: bool = False) -> int:
