@@ -204,6 +204,29 @@ int ikbo_request_attention(const void *q_req, int64_t num_req, int32_t q_len, co
                            void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* ------------------------------------------------------------------------------------------
+ * GLM factorization machine, two groups (Sec. 3.1.4, Eq. 9 with the block mask, two-group form
+ * Eq. 10): pairwise inner products of feature embeddings, masked so the request group sees only
+ * request features:
+ *   y_req[r]  = X^R_r (X^R_r)^T                                    [n_req_feat, n_req_feat]
+ *   y_cand[c] = [ X^C_c (X^R_{m(c)})^T ,  X^C_c (X^C_c)^T ]        [n_cand_feat, n_req_feat + n_cand_feat]
+ * The request embeddings are read through the candidate->request index inside the kernel
+ * (never expanded to the candidate batch).
+ * x_req  [num_req, n_req_feat, dim], x_cand [num_cand, n_cand_feat, dim]      (in_dtype)
+ * y_req  [num_req, n_req_feat, n_req_feat] (out_dtype) or NULL to skip the request group
+ * y_cand [num_cand, n_cand_feat, n_req_feat + n_cand_feat]                   (out_dtype)
+ * cand_to_req, req_cand_offsets, index_flags: see the conventions above (offsets, when given,
+ *        define each candidate's request); a candidate without a valid request gets zeros.
+ * n_req_feat, n_cand_feat: multiples of 4 (else IKBO_UNSUPPORTED); dim >= 1. bf16 with dim in
+ *        {32, 64, 128} and both feature counts <= 64 runs on MFMA; other shapes run a plain
+ *        fp32-arithmetic kernel.
+ * No workspace. Errors: IKBO_INVALID_ARGUMENT, IKBO_UNSUPPORTED, IKBO_MISALIGNED, IKBO_HIP_ERROR.
+ * ---------------------------------------------------------------------------------------- */
+int ikbo_fm_forward(const void *x_req, int64_t num_req, int32_t n_req_feat,
+                    const void *x_cand, int64_t num_cand, int32_t n_cand_feat, int32_t dim,
+                    const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                    int32_t in_dtype, int32_t out_dtype, void *y_req, void *y_cand, void *hip_stream);
+
+/* ------------------------------------------------------------------------------------------
  * Index check: counts, on the device, (a) candidates whose cand_to_req is outside
  * [0, num_req), (b) with IKBO_INDEX_SORTED, candidates whose map value is below the previous
  * candidate's, (c) when both arrays are given, candidates that are not inside

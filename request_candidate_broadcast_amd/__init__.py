@@ -55,7 +55,8 @@ EXPORTS = ["ikbo_version", "ikbo_status_string", "ikbo_last_error_message",
            "ikbo_dca_workspace_size", "ikbo_dca_forward",
            "ikbo_lcb_workspace_size", "ikbo_lcb_forward",
            "ikbo_glm_mlp_workspace_size", "ikbo_glm_mlp_forward", "ikbo_check_index",
-           "ikbo_kv_project", "ikbo_request_attention_workspace_size", "ikbo_request_attention"]
+           "ikbo_kv_project", "ikbo_request_attention_workspace_size", "ikbo_request_attention",
+           "ikbo_fm_forward"]
 
 _lib = None
 
@@ -98,6 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ikbo_kv_project.argtypes = [vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, vp]
     lib.ikbo_request_attention_workspace_size.restype = sz
     lib.ikbo_request_attention_workspace_size.argtypes = [i64]
+    lib.ikbo_fm_forward.restype = ctypes.c_int
+    lib.ikbo_fm_forward.argtypes = [vp, i64, i32, vp, i64, i32, i32, vp, vp, u32, i32, i32, vp, vp, vp]
     lib.ikbo_request_attention.restype = ctypes.c_int
     lib.ikbo_request_attention.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, i32, f32, i32, i32, vp, vp, sz, vp]
     _lib = lib
@@ -208,6 +211,37 @@ def ikbo_dca_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, num_r
 
 
 # ------------------------------------------------------------------------------------------------
+def ikbo_fm_forward(x_req: torch.Tensor, x_cand: torch.Tensor, *, cand_to_req: Optional[torch.Tensor] = None,
+                    req_cand_offsets: Optional[torch.Tensor] = None, sorted_index: bool = False, out_dtype=None,
+                    want_request_output: bool = True, y_req: Optional[torch.Tensor] = None,
+                    y_cand: Optional[torch.Tensor] = None, stream=None):
+    """GLM factorization machine (two groups). x_req [R, n_r, d], x_cand [C, n_c, d].
+    Returns (y_req [R, n_r, n_r] or None, y_cand [C, n_c, n_r + n_c]) in out_dtype (default: input dtype)."""
+    lib = load_library()
+    _need_contig("x_req", x_req)
+    _need_contig("x_cand", x_cand)
+    R, n_r, d = x_req.shape
+    C, n_c, d2 = x_cand.shape
+    if d2 != d:
+        raise ValueError("x_req and x_cand must share the embedding width")
+    cand_to_req = _index(cand_to_req, "cand_to_req")
+    req_cand_offsets = _index(req_cand_offsets, "req_cand_offsets")
+    in_code = _dt(x_req)
+    out_code = in_code if out_dtype is None else _dt(torch.empty(0, dtype=out_dtype))
+    dev = x_cand.device
+    if y_cand is None:
+        y_cand = torch.empty((C, n_c, n_r + n_c), dtype=_torch_dtype(out_code), device=dev)
+    if want_request_output and y_req is None:
+        y_req = torch.empty((R, n_r, n_r), dtype=_torch_dtype(out_code), device=dev)
+    if not want_request_output:
+        y_req = None
+    st = lib.ikbo_fm_forward(_ptr(x_req), R, n_r, _ptr(x_cand), C, n_c, d, _ptr(cand_to_req), _ptr(req_cand_offsets),
+                             IKBO_INDEX_SORTED if sorted_index else 0, in_code, _dt(y_cand), _ptr(y_req), _ptr(y_cand),
+                             _stream(stream))
+    _check(st)
+    return y_req, y_cand
+
+
 def ikbo_request_attention_workspace_size(num_req: int) -> int:
     return int(load_library().ikbo_request_attention_workspace_size(num_req))
 

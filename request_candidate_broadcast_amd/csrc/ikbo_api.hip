@@ -405,6 +405,49 @@ int ikbo_request_attention(const void *q_req, int64_t num_req, int32_t q_len, co
                    in_dtype, out_dtype, out, rest, s);
 }
 
+// ---- GLM factorization machine -------------------------------------------------------------------
+int ikbo_fm_forward(const void *x_req, int64_t num_req, int32_t n_req_feat, const void *x_cand, int64_t num_cand,
+                    int32_t n_cand_feat, int32_t dim, const int32_t *cand_to_req, const int32_t *req_cand_offsets,
+                    uint32_t index_flags, int32_t in_dtype, int32_t out_dtype, void *y_req, void *y_cand,
+                    void *hip_stream) {
+    const int64_t R = num_req, C = num_cand;
+    if (R < 0 || C < 0 || n_req_feat < 0 || n_cand_feat < 0 || dim <= 0)
+        return fail(IKBO_INVALID_ARGUMENT, "bad sizes (num_req %lld num_cand %lld n_req_feat %d n_cand_feat %d dim %d)",
+                    (long long)R, (long long)C, n_req_feat, n_cand_feat, dim);
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(IKBO_UNSUPPORTED, "dtype in %d out %d", in_dtype, out_dtype);
+    if (n_req_feat % 4 || n_cand_feat % 4)
+        return fail(IKBO_UNSUPPORTED, "feature counts must be multiples of 4 (got %d, %d)", n_req_feat, n_cand_feat);
+    int rc = check_index_args(cand_to_req, req_cand_offsets, index_flags, C);
+    if (rc) return rc;
+    const bool want_req = y_req != nullptr && R > 0 && n_req_feat > 0;
+    if (C > 0 && (n_cand_feat > 0) && (!x_cand || !y_cand))
+        return fail(IKBO_INVALID_ARGUMENT, "x_cand and y_cand must be non-NULL when num_cand > 0");
+    if ((want_req || (C > 0 && n_req_feat > 0)) && R > 0 && !x_req)
+        return fail(IKBO_INVALID_ARGUMENT, "x_req is NULL");
+    const void *ptrs[] = {x_req, x_cand, y_req, y_cand};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    if (C * (int64_t)n_cand_feat * (n_req_feat + n_cand_feat) > (1LL << 62))
+        return fail(IKBO_UNSUPPORTED, "output too large");
+    if ((C == 0 || n_cand_feat == 0) && !want_req) return ok();
+    ikbo::FmArgs a = {};
+    a.x_r = x_req;
+    a.x_c = x_cand;
+    a.y_r = want_req ? y_req : nullptr;
+    a.y_c = y_cand;
+    a.R = R;
+    a.C = n_cand_feat > 0 ? C : 0;
+    a.n_r = n_req_feat;
+    a.n_c = n_cand_feat;
+    a.d = dim;
+    a.map = cand_to_req;
+    a.off = req_cand_offsets;
+    a.in_f32 = in_dtype == IKBO_F32;
+    a.out_f32 = out_dtype == IKBO_F32;
+    IKBO_HIP(ikbo::launch_fm(a, (hipStream_t)hip_stream));
+    return ok();
+}
+
 // ---- K/V projection -----------------------------------------------------------------------------
 int ikbo_kv_project(const void *s_rows, int64_t rows, int32_t d_in, const void *w_k, const void *w_v, int32_t d_out,
                     int32_t in_dtype, int32_t out_dtype, void *k_out, void *v_out, void *hip_stream) {

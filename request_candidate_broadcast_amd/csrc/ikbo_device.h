@@ -100,6 +100,13 @@ __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_wave_ba
 }
 
 // A pointer that is the same in every lane, moved to scalar registers.
+// A 64-bit value every lane holds alike, in scalar registers (branches on it are uniform)
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 template <typename T>
 __device__ __forceinline__ T *uniform_ptr(T *p) {
     const uint64_t u = (uint64_t)p;

@@ -755,11 +755,6 @@ __device__ __forceinline__ void flag_release(int32_t *p, int32_t v) {
 // with a loop exit that the compiler takes as divergent (a value read from LDS into a vector
 // register), it may run the loop for the other lanes while the one lane that claims items and
 // sets flags waits outside it, and the workgroup never ends.
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 // lane 0 of the calling wave applies op, every lane gets its result (call with all lanes active)
 template <typename Op>
 __device__ __forceinline__ int32_t lane0(int lane, Op op) {

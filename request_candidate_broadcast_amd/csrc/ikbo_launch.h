@@ -110,4 +110,18 @@ int64_t lcb_fused_sync_ints(int64_t M, int32_t N);
 bool lcb_fused_supported(const GemmArgs &req, const GemmArgs &cand);
 hipError_t launch_lcb_fused(const LcbFusedArgs &f, hipStream_t s);
 
+// ---- GLM factorization machine (ikbo_fm.hip) -----------------------------------------------------
+struct FmArgs {
+    const void *x_r, *x_c;      // [R, n_r, d], [C, n_c, d]
+    void *y_r, *y_c;            // [R, n_r, n_r] or null, [C, n_c, n_r + n_c]
+    int64_t R, C;
+    int32_t n_r, n_c, d;
+    const int32_t *map, *off;   // candidate -> request; offsets [R + 1] take precedence when set
+    int32_t in_f32, out_f32;
+    int64_t chunk;              // items per wave (set by launch_fm)
+};
+// whether launch_fm takes the MFMA path (bf16, d in {32, 64, 128}, n_r and n_c <= 64)
+bool fm_mfma_supported(const FmArgs &a);
+hipError_t launch_fm(const FmArgs &a, hipStream_t s);
+
 }  // namespace ikbo

@@ -195,3 +195,23 @@ def test_request_attention_argument_errors(lib):
     assert rattn(lib, q=MIS) == ikbo.IKBO_MISALIGNED
     assert rattn(lib, Lq=0) == ikbo.IKBO_INVALID_ARGUMENT
     assert rattn(lib, R=0) == ikbo.IKBO_OK
+
+
+def fm(lib, **kw):
+    a = dict(xr=FAKE, R=4, nr=32, xc=FAKE, C=64, nc=32, d=64, m=FAKE, off=None, flags=0, ind=1, outd=1, yr=FAKE,
+             yc=FAKE, stream=None)
+    a.update(kw)
+    return lib.ikbo_fm_forward(a["xr"], a["R"], a["nr"], a["xc"], a["C"], a["nc"], a["d"], a["m"], a["off"], a["flags"],
+                               a["ind"], a["outd"], a["yr"], a["yc"], a["stream"])
+
+
+def test_fm_argument_errors(lib):
+    assert fm(lib, d=0) == ikbo.IKBO_INVALID_ARGUMENT
+    assert fm(lib, nr=30) == ikbo.IKBO_UNSUPPORTED
+    assert b"multiples of 4" in lib.ikbo_last_error_message()
+    assert fm(lib, ind=5) == ikbo.IKBO_UNSUPPORTED
+    assert fm(lib, m=None, off=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert fm(lib, yc=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert fm(lib, xr=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert fm(lib, yc=MIS) == ikbo.IKBO_MISALIGNED
+    assert fm(lib, C=0, yr=None) == ikbo.IKBO_OK       # nothing to compute
