@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "IKBO-DCA TFLOP/s + ms; IKBO-LCB ms; % of MI355X bf16 MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+FM_SHAPE = (128, 2048, 32, 32, 64)   # requests, candidates per request, n_r, n_c, d
 
 
 def parse():
@@ -33,7 +34,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="block", choices=["block", "layer", "dca_fixed", "dca_ragged", "lcb"])
+    p.add_argument("--workload", default="block", choices=["block", "layer", "dca_fixed", "dca_ragged", "lcb", "fm"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=0, help="candidates in the oracle sample (0 = default)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -174,6 +175,29 @@ def main():
                 names = [("mlp", 0, 1), ("kv_proj_c", 1, 2), ("dca", 2, 3), ("kv_proj_r", 3, 4), ("attn_r", 4, 5)]
                 config = dict(config, workload="ROCS DCA layer: GLM-MLP -> K/V projections of S (once per request) "
                               "-> A^C (IKBO-DCA) + A^R (request-side attention)", seq_width=d_in)
+        elif args.workload == "fm":
+            # GLM factorization machine (Eq. 10) on the block's batch: 128 requests x 2048 candidates,
+            # 32 request and 32 candidate features of width 64, N(0,1), bf16 in and out
+            R, per_r, n_r, n_c, d = FM_SHAPE
+            C = R * per_r
+            fm_counts = np.full(R, per_r)
+            x_r = up(synth.draw(0, 80, R * n_r * d, "bf16").reshape(R, n_r, d))
+            x_c = up(synth.draw(0, 81, C * n_c * d, "bf16").reshape(C, n_c, d))
+            off = up(synth.offsets_from_counts(fm_counts))
+            y_r = torch.empty((R, n_r, n_r), dtype=torch.bfloat16, device=dev)
+            y_c = torch.empty((C, n_c, n_r + n_c), dtype=torch.bfloat16, device=dev)
+            flops["fm"] = 2.0 * C * n_c * (n_r + n_c) * d + 2.0 * R * n_r * n_r * d
+            algo_bytes["fm"] = 2 * (C * n_c * d + C * n_c * (n_r + n_c) + R * n_r * d + R * n_r * n_r) + 4 * (R + 1)
+
+            def step(ev):
+                ev[0].record(stream)
+                ikbo.ikbo_fm_forward(x_r, x_c, req_cand_offsets=off, y_req=y_r, y_cand=y_c, stream=stream)
+                ev[1].record(stream)
+
+            names = [("fm", 0, 1)]
+            dominant = "fm"
+            config = {"workload": "GLM factorization machine (two groups, in-kernel broadcast)", "requests": R,
+                      "candidates": C, "n_req_feat": n_r, "n_cand_feat": n_c, "dim": d}
         elif args.workload in ("dca_fixed", "dca_ragged"):
             s = synth.dca_spec(args.workload)
             q = up(synth.dca_q(s))
@@ -276,7 +300,14 @@ def main():
                 traffic = ent.get("bytes_per_launch")
     except (OSError, ValueError, KeyError):
         traffic = None
-    roofline = {"bound": "mfma", "achieved": round(dk["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+    if dominant == "fm":      # HBM-bound (about 32 FLOP per byte at bf16 in and out)
+        gbs = dk["gbs_algorithmic"]
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dominant,
+                    "bytes_per_launch": algo_bytes[dominant], "ms_per_launch": round(dk["ms_avg"], 4)}
+    else:
+        roofline = None
+    roofline = roofline or {"bound": "mfma", "achieved": round(dk["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(dk["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": dominant, "flops_per_launch": flops[dominant], "ms_per_launch": round(dk["ms_avg"], 4)}
 
@@ -356,6 +387,20 @@ def cpu_baseline(args, np):
             secs += time.perf_counter() - t1
             work += 4 * 2.0 * s.L * d_in * hd + 4.0 * s.Lq * s.H * s.d * s.L
             sample += "; plus the four K/V projections of request %d's %d sequence rows and its A^R" % (r0, s.L)
+    elif args.workload == "fm":
+        R, per_r, n_r, n_c, d = FM_SHAPE
+        # every request and all their candidates: the whole workload (a few seconds of oracle work)
+        reqs = list(range(R))
+        n_per = min(per_r, args.cpu_sample // len(reqs)) if args.cpu_sample else per_r
+        x_r = synth.draw(0, 80, R * n_r * d, "bf16").reshape(R, n_r, d)
+        x_c = np.concatenate([synth.draw(0, 81, n_per * n_c * d, "bf16", start=r * per_r * n_c * d)
+                              for r in reqs]).reshape(-1, n_c, d)
+        m_sub = np.repeat(np.array(reqs, np.int32), n_per)
+        t0 = time.perf_counter()
+        oracle.fm(x_r, x_c, m=m_sub)
+        secs = time.perf_counter() - t0
+        work = 2.0 * len(m_sub) * n_c * (n_r + n_c) * d
+        sample = "%d candidates (the first %d of each of the %d requests)" % (len(m_sub), n_per, len(reqs))
     elif args.workload in ("dca_fixed", "dca_ragged"):
         s = synth.dca_spec(args.workload)
         reqs = [0, 1, s.R // 2, s.R - 1]

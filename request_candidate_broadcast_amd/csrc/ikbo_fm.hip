@@ -12,7 +12,11 @@
 // d/16 chunks of 8, chunk e feeding k step e: the same permutation of the contraction index on both
 // operands, so the products summed are the definition's. The candidate's own fragments are both
 // operands of the X^C (X^C)^T block. The workload is HBM-bound (d/2 FLOP per byte at bf16 in, bf16
-// out), so the design is about streaming: small register footprint, many waves per CU.
+// out), so the design is about streaming: small register footprint, many waves per CU. Results go
+// through a per-wave LDS stage: the 32 x W row block of an output is written there from the
+// accumulators, then stored as whole rows, consecutive lanes on consecutive 16-byte chunks, so the
+// L2 receives full-line writes (stored straight from the accumulator layout, each instruction
+// would write 16 bytes into each of 32 rows: four times the write requests).
 #include "ikbo_device.h"
 #include "ikbo_launch.h"
 
@@ -36,20 +40,53 @@ __device__ __forceinline__ void fm_rows(const uint16_t *x, int nrows, int l32, i
     }
 }
 
-// One 32 x 32 block of an output, rows row0 + l32 (< nrows) and columns col0 + 8 jj + 4 half + {0..3}
-// (< ncols, a multiple of 4) of an output matrix with row stride W at element offset base.
-__device__ __forceinline__ void fm_store(void *y, int out_f32, int64_t base, int W, int row, int nrows, int col0,
-                                         int ncols, int half, const f32x16 &acc) {
-    if (row >= nrows) return;
+// One 32 x 32 accumulator block into the wave's LDS stage (fp32, row stride SW floats): lane
+// (l32, half) holds row l32, columns col0 + 8 jj + 4 half + {0..3}; columns past ncols (a multiple
+// of 4) are skipped.
+__device__ __forceinline__ void fm_stage(float *st, int SW, int l32, int half, int col0, int ncols, const f32x16 &acc) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
         const int col = 8 * jj + 4 * half;
-        if (col >= ncols) continue;
-        const int64_t o = base + (int64_t)row * W + col0 + col;
-        if (out_f32) *(float4 *)((float *)y + o) = make_float4(acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]);
-        else *(uint2 *)((uint16_t *)y + o) = make_uint2(pack_bf16x2(acc[4 * jj], acc[4 * jj + 1]),
-                                                         pack_bf16x2(acc[4 * jj + 2], acc[4 * jj + 3]));
+        if (col < ncols)
+            *(float4 *)(st + l32 * SW + col0 + col) = make_float4(acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]);
     }
+}
+
+// Rows [0, nrows) (at most 32) of the stage, W columns each (a multiple of 4), to the output at
+// element offset base with row stride W: consecutive lanes take consecutive chunks (16 bytes, or 8
+// for bf16 rows whose length is not a multiple of 8, which keeps every store naturally aligned).
+// The stage is written by other lanes of the same wave: wavefront-scope fences on both sides keep
+// the compiler from moving these reads above those writes or the next block's writes above them.
+__device__ __forceinline__ void fm_flush(const float *st, int SW, void *y, int out_f32, int64_t base, int W, int nrows,
+                                         int lane) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (out_f32) {
+        const int cpr = W / 4;
+        for (int i = lane; i < nrows * cpr; i += 64) {
+            const int row = i / cpr, q = i - row * cpr;
+            *(float4 *)((float *)y + base + (int64_t)row * W + 4 * q) = *(const float4 *)(st + row * SW + 4 * q);
+        }
+    } else if (W % 8 == 0) {
+        const int cpr = W / 8;
+        for (int i = lane; i < nrows * cpr; i += 64) {
+            const int row = i / cpr, q = i - row * cpr;
+            const float4 u = *(const float4 *)(st + row * SW + 8 * q);
+            const float4 v = *(const float4 *)(st + row * SW + 8 * q + 4);
+            *(uint4 *)((uint16_t *)y + base + (int64_t)row * W + 8 * q) =
+                make_uint4(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        }
+    } else {
+        const int cpr = W / 4;
+        for (int i = lane; i < nrows * cpr; i += 64) {
+            const int row = i / cpr, q = i - row * cpr;
+            const float4 u = *(const float4 *)(st + row * SW + 4 * q);
+            *(uint2 *)((uint16_t *)y + base + (int64_t)row * W + 4 * q) =
+                make_uint2(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w));
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 }
 
 __device__ __forceinline__ void fm_zero(void *y, int out_f32, int64_t base, int64_t n, int lane) {
@@ -87,6 +124,8 @@ template <int KS, int NB, int WPE>
 __global__ __launch_bounds__(kFmWaves * 64) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void fm_bf16_kernel(FmArgs a) {
     constexpr int D = 16 * KS;
     constexpr int kFmMaxBlocks = NB;
+    constexpr int SW = 64 * NB + 4;                        // stage row stride (floats): W <= 64 NB
+    __shared__ float stage_all[kFmWaves][32 * SW];
     const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
     const int64_t wave = (int64_t)blockIdx.x * kFmWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t items = a.C + (a.y_r ? a.R : 0);
@@ -94,6 +133,7 @@ __global__ __launch_bounds__(kFmWaves * 64) __attribute__((amdgpu_waves_per_eu(W
     const int rbr = (a.n_r + 31) / 32, rbc = (a.n_c + 31) / 32;
     const int W = a.n_r + a.n_c;
     const uint16_t *xr = (const uint16_t *)a.x_r, *xc = (const uint16_t *)a.x_c;
+    float *st = stage_all[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
     bf16x8 fr[kFmMaxBlocks][KS], fc[kFmMaxBlocks][KS];
     int64_t have_r = -1, cursor = -1;
     for (int64_t it = i0; it < i1; ++it) {
@@ -126,7 +166,7 @@ __global__ __launch_bounds__(kFmWaves * 64) __attribute__((amdgpu_waves_per_eu(W
                     for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
 #pragma unroll
                     for (int e = 0; e < KS; ++e) acc = mfma_32x32x16_bf16(fr[cb][e], fc[rb][e], acc);
-                    fm_store(a.y_c, a.out_f32, base, W, 32 * rb + l32, a.n_c, 32 * cb, a.n_r - 32 * cb, half, acc);
+                    fm_stage(st, SW, l32, half, 32 * cb, a.n_r - 32 * cb, acc);
                 }
                 // candidate-candidate block(s): columns [n_r, n_r + n_c)
 #pragma unroll
@@ -137,9 +177,9 @@ __global__ __launch_bounds__(kFmWaves * 64) __attribute__((amdgpu_waves_per_eu(W
                     for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
 #pragma unroll
                     for (int e = 0; e < KS; ++e) acc = mfma_32x32x16_bf16(fc[cb][e], fc[rb][e], acc);
-                    fm_store(a.y_c, a.out_f32, base, W, 32 * rb + l32, a.n_c, a.n_r + 32 * cb, a.n_c - 32 * cb, half,
-                             acc);
+                    fm_stage(st, SW, l32, half, a.n_r + 32 * cb, a.n_c - 32 * cb, acc);
                 }
+                fm_flush(st, SW, a.y_c, a.out_f32, base + (int64_t)32 * rb * W, W, min(32, a.n_c - 32 * rb), lane);
             }
         } else {
             // request group: y_r[r] = X^R_r (X^R_r)^T
@@ -160,8 +200,9 @@ __global__ __launch_bounds__(kFmWaves * 64) __attribute__((amdgpu_waves_per_eu(W
                     for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
 #pragma unroll
                     for (int e = 0; e < KS; ++e) acc = mfma_32x32x16_bf16(fr[cb][e], fr[rb][e], acc);
-                    fm_store(a.y_r, a.out_f32, base, a.n_r, 32 * rb + l32, a.n_r, 32 * cb, a.n_r - 32 * cb, half, acc);
+                    fm_stage(st, SW, l32, half, 32 * cb, a.n_r - 32 * cb, acc);
                 }
+                fm_flush(st, SW, a.y_r, a.out_f32, base + (int64_t)32 * rb * a.n_r, a.n_r, min(32, a.n_r - 32 * rb), lane);
             }
         }
     }
@@ -234,7 +275,7 @@ hipError_t launch_fm(const FmArgs &a0, hipStream_t s) {
 #define IKBO_FM(KS, NB, WPE) hipLaunchKernelGGL((fm_bf16_kernel<KS, NB, WPE>), dim3((unsigned)grid), dim3(kFmWaves * 64), 0, s, a)
         if (a.d == 32) {
             if (one) IKBO_FM(2, 1, 4);
-            else IKBO_FM(2, 2, 4);
+            else IKBO_FM(2, 2, 2);
         } else if (a.d == 64) {
             if (one) IKBO_FM(4, 1, 4);
             else IKBO_FM(4, 2, 2);
