@@ -20,6 +20,10 @@ then evaluates the definitions:
 * ``fm``    the GLM factorization machine, Sec. 3.1.4 Eq. 9-10 (two groups): request outputs
             X^R (X^R)^T, candidate outputs [X^C (X^R_m)^T, X^C (X^C)^T], in fp64 with the request
             rows expanded per candidate.
+* ``lcb_emb`` the ROCSified LCB in its embedding-matrix (row-axis) form, Sec. 3.1.2 Eq. 5-6 (two
+            groups): Y^R = W_RR X^R, Y^C = W_CR X^R_m + W_CC X^C, followed by the group-local
+            normalisation of Sec. 3.1.3 Eq. 7 (LayerNorm or RMSNorm of each embedding row), in
+            fp64 with the request embeddings expanded per candidate.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py`` against library
 routines, closed forms, invariants and brute force on tiny inputs.
@@ -251,6 +255,62 @@ def fm(x_r: np.ndarray, x_c: np.ndarray, *, m=None, off=None, cands: Optional[Se
     out = {"y_c": y_c}
     if want_request:
         out["y_r"] = np.stack([xr[r] @ xr[r].T for r in range(R)]) if R else np.zeros((0, n_r, n_r))
+    return out
+
+
+NORM = {"none": 0, "layer": 1, "rms": 2}
+
+
+def _group_norm(y: np.ndarray, kind: str, gamma, beta, eps: float) -> np.ndarray:
+    """Eq. 7 on one group's output: each embedding row (last axis, width d) normalised on its own
+    values only. "layer": (y - mean) / sqrt(var + eps) with the biased variance; "rms":
+    y / sqrt(mean(y^2) + eps); then * gamma + beta (gamma = 1, beta = 0 when None)."""
+    if kind == "none":
+        return y
+    if kind == "layer":
+        mu = y.mean(axis=-1, keepdims=True)
+        var = ((y - mu) ** 2).mean(axis=-1, keepdims=True)
+        z = (y - mu) / np.sqrt(var + eps)
+    elif kind == "rms":
+        z = y / np.sqrt((y ** 2).mean(axis=-1, keepdims=True) + eps)
+    else:
+        raise ValueError("norm must be one of %s" % sorted(NORM))
+    if gamma is not None:
+        z = z * np.asarray(gamma, dtype=np.float64)
+    if beta is not None:
+        z = z + np.asarray(beta, dtype=np.float64)
+    return z
+
+
+def lcb_emb(x_r: np.ndarray, x_c: np.ndarray, w_rr: np.ndarray, w_cr: np.ndarray, w_cc: np.ndarray, *,
+            m=None, off=None, norm: str = "none", gamma_r=None, beta_r=None, gamma_c=None, beta_c=None,
+            eps: float = 1e-5, cands: Optional[Sequence[int]] = None, want_request: bool = False,
+            chunk: int = 4096):
+    """ROCSified LCB, embedding form (Eq. 5-6, two groups), then the group-local norm (Eq. 7).
+
+    x_r [R, n_r, d], x_c [C, n_c, d]; w_rr [k_r, n_r], w_cr [k_c, n_r], w_cc [k_c, n_c] (bf16 bits
+    or fp32, all of one kind); gamma_*/beta_* fp32 [d] or None. Returns {"y_c": [n, k_c, d]} for
+    the candidates `cands` (all when None) and, with want_request, "y_r": [R, k_r, d]. A candidate
+    whose request is out of range (or not covered by the offsets) gets zeros."""
+    xr, xc = decode(x_r), decode(x_c)
+    wrr, wcr, wcc = decode(w_rr), decode(w_cr), decode(w_cc)
+    R = xr.shape[0]
+    ids = np.arange(xc.shape[0]) if cands is None else np.asarray(cands, dtype=np.int64)
+    mm, oo = _i32(m), _i32(off)
+    req = np.array([_get().oracle_request_of(_ptr(mm), _ptr(oo), R, int(c)) for c in ids], dtype=np.int64)
+    y_c = np.zeros((len(ids), wcc.shape[0], xc.shape[2]), dtype=np.float64)
+    for s in range(0, len(ids), chunk):
+        sl = slice(s, s + chunk)
+        ok = req[sl] >= 0
+        if not np.any(ok):
+            continue
+        rows = np.arange(s, min(s + chunk, len(ids)))[ok]
+        x_req = xr[req[rows]]                       # the request embeddings expanded per candidate
+        y = wcr @ x_req + wcc @ xc[ids[rows]]       # Eq. 6, candidate rows: W_CR X^R + W_CC X^C
+        y_c[rows] = _group_norm(y, norm, gamma_c, beta_c, eps)
+    out = {"y_c": y_c}
+    if want_request:
+        out["y_r"] = _group_norm(wrr @ xr, norm, gamma_r, beta_r, eps)   # Eq. 6, request rows: W_RR X^R
     return out
 
 
