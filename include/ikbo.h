@@ -57,6 +57,11 @@ extern "C" {
 #define IKBO_ACT_NONE 0
 #define IKBO_ACT_GELU 1             /* exact form x * Phi(x) = x/2 (1 + erf(x / sqrt 2)) */
 
+/* Group-local normalisations (Sec. 3.1.3, Eq. 7), of each embedding row over its d values */
+#define IKBO_NORM_NONE 0
+#define IKBO_NORM_LAYER 1           /* (y - mean) / sqrt(var + eps), biased variance; then * gamma + beta */
+#define IKBO_NORM_RMS 2             /* y / sqrt(mean(y^2) + eps); then * gamma + beta */
+
 /* index_flags bits */
 #define IKBO_INDEX_SORTED 1u        /* cand_to_req is non-decreasing (candidates grouped) */
 
@@ -225,6 +230,42 @@ int ikbo_fm_forward(const void *x_req, int64_t num_req, int32_t n_req_feat,
                     const void *x_cand, int64_t num_cand, int32_t n_cand_feat, int32_t dim,
                     const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
                     int32_t in_dtype, int32_t out_dtype, void *y_req, void *y_cand, void *hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * LCB in its embedding-matrix (row-axis) form, two groups (Sec. 3.1.2, Eq. 5 and the block
+ * form Eq. 6), each group's output then normalised on its own (Sec. 3.1.3, Eq. 7):
+ *   y_req[r]  = Norm_R( W_RR X^R_r )                                   [n_req_out, dim]
+ *   y_cand[c] = Norm_C( W_CR X^R_{m(c)} + W_CC X^C_c )                 [n_cand_out, dim]
+ * The request-derived term W_CR X^R_r is computed once per request into the workspace (fp32) and
+ * added in the candidate kernel through the candidate->request index (never expanded to the
+ * candidate batch). Norm acts on each output row (one embedding) over its dim values.
+ * x_req  [num_req, n_req_in, dim], x_cand [num_cand, n_cand_in, dim]           (in_dtype)
+ * w_rr   [n_req_out, n_req_in], w_cr [n_cand_out, n_req_in], w_cc [n_cand_out, n_cand_in] (in_dtype)
+ * norm   IKBO_NORM_NONE | IKBO_NORM_LAYER | IKBO_NORM_RMS; eps >= 0 (added to the variance or the
+ *        mean square; 0 gives inf/NaN on a constant or zero row, as the formula does).
+ * gamma_req, beta_req, gamma_cand, beta_cand: fp32 [dim] or NULL (gamma 1, beta 0); used only
+ *        when norm is not IKBO_NORM_NONE.
+ * y_req  [num_req, n_req_out, dim] (out_dtype) or NULL to skip the request group
+ * y_cand [num_cand, n_cand_out, dim] (out_dtype); a candidate without a valid request gets zeros.
+ * cand_to_req, req_cand_offsets, index_flags: see the conventions above.
+ * n_req_in, n_cand_in >= 1; 1 <= dim <= 256. bf16 with dim in {32, 64, 128} and n_cand_in,
+ *        n_cand_out <= 64 runs the candidates on MFMA; other shapes run plain fp32-arithmetic
+ *        kernels. The request group always runs the plain kernel (num_req rows only).
+ * workspace >= ikbo_lcb_emb_workspace_size(num_req, n_cand_out, dim) bytes when the candidate
+ *        group is computed (num_cand > 0 and n_cand_out > 0), else unused.
+ * Errors: IKBO_INVALID_ARGUMENT, IKBO_UNSUPPORTED, IKBO_MISALIGNED, IKBO_WORKSPACE_TOO_SMALL,
+ *         IKBO_HIP_ERROR.
+ * ---------------------------------------------------------------------------------------- */
+size_t ikbo_lcb_emb_workspace_size(int64_t num_req, int32_t n_cand_out, int32_t dim);
+
+int ikbo_lcb_emb_forward(const void *x_req, int64_t num_req, int32_t n_req_in,
+                         const void *x_cand, int64_t num_cand, int32_t n_cand_in, int32_t dim,
+                         const void *w_rr, int32_t n_req_out, const void *w_cr, const void *w_cc,
+                         int32_t n_cand_out, const int32_t *cand_to_req, const int32_t *req_cand_offsets,
+                         uint32_t index_flags, int32_t norm, const float *gamma_req, const float *beta_req,
+                         const float *gamma_cand, const float *beta_cand, float eps, int32_t in_dtype,
+                         int32_t out_dtype, void *y_req, void *y_cand, void *workspace,
+                         size_t workspace_bytes, void *hip_stream);
 
 /* ------------------------------------------------------------------------------------------
  * Index check: counts, on the device, (a) candidates whose cand_to_req is outside

@@ -28,6 +28,7 @@ IKBO_OK, IKBO_INVALID_ARGUMENT, IKBO_UNSUPPORTED, IKBO_MISALIGNED, IKBO_WORKSPAC
 IKBO_F32, IKBO_BF16 = 0, 1
 IKBO_ACT_NONE, IKBO_ACT_GELU = 0, 1
 IKBO_INDEX_SORTED = 1
+IKBO_NORM_NONE, IKBO_NORM_LAYER, IKBO_NORM_RMS = 0, 1, 2
 
 ACTIVATIONS = {"none": IKBO_ACT_NONE, "gelu": IKBO_ACT_GELU, None: IKBO_ACT_NONE}
 
@@ -56,7 +57,7 @@ EXPORTS = ["ikbo_version", "ikbo_status_string", "ikbo_last_error_message",
            "ikbo_lcb_workspace_size", "ikbo_lcb_forward",
            "ikbo_glm_mlp_workspace_size", "ikbo_glm_mlp_forward", "ikbo_check_index",
            "ikbo_kv_project", "ikbo_request_attention_workspace_size", "ikbo_request_attention",
-           "ikbo_fm_forward"]
+           "ikbo_fm_forward", "ikbo_lcb_emb_workspace_size", "ikbo_lcb_emb_forward"]
 
 _lib = None
 
@@ -101,6 +102,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ikbo_request_attention_workspace_size.argtypes = [i64]
     lib.ikbo_fm_forward.restype = ctypes.c_int
     lib.ikbo_fm_forward.argtypes = [vp, i64, i32, vp, i64, i32, i32, vp, vp, u32, i32, i32, vp, vp, vp]
+    lib.ikbo_lcb_emb_workspace_size.restype = sz
+    lib.ikbo_lcb_emb_workspace_size.argtypes = [i64, i32, i32]
+    lib.ikbo_lcb_emb_forward.restype = ctypes.c_int
+    lib.ikbo_lcb_emb_forward.argtypes = [vp, i64, i32, vp, i64, i32, i32, vp, i32, vp, vp, i32, vp, vp, u32, i32,
+                                         vp, vp, vp, vp, f32, i32, i32, vp, vp, vp, sz, vp]
     lib.ikbo_request_attention.restype = ctypes.c_int
     lib.ikbo_request_attention.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, i32, f32, i32, i32, vp, vp, sz, vp]
     _lib = lib
@@ -238,6 +244,61 @@ def ikbo_fm_forward(x_req: torch.Tensor, x_cand: torch.Tensor, *, cand_to_req: O
     st = lib.ikbo_fm_forward(_ptr(x_req), R, n_r, _ptr(x_cand), C, n_c, d, _ptr(cand_to_req), _ptr(req_cand_offsets),
                              IKBO_INDEX_SORTED if sorted_index else 0, in_code, _dt(y_cand), _ptr(y_req), _ptr(y_cand),
                              _stream(stream))
+    _check(st)
+    return y_req, y_cand
+
+
+def ikbo_lcb_emb_workspace_size(num_req: int, n_cand_out: int, dim: int) -> int:
+    return int(load_library().ikbo_lcb_emb_workspace_size(num_req, n_cand_out, dim))
+
+
+_NORMS = {"none": IKBO_NORM_NONE, "layer": IKBO_NORM_LAYER, "rms": IKBO_NORM_RMS}
+
+
+def ikbo_lcb_emb_forward(x_req: torch.Tensor, x_cand: torch.Tensor, w_rr: torch.Tensor, w_cr: torch.Tensor,
+                         w_cc: torch.Tensor, *, cand_to_req: Optional[torch.Tensor] = None,
+                         req_cand_offsets: Optional[torch.Tensor] = None, sorted_index: bool = False,
+                         norm: str = "none", gamma_req: Optional[torch.Tensor] = None,
+                         beta_req: Optional[torch.Tensor] = None, gamma_cand: Optional[torch.Tensor] = None,
+                         beta_cand: Optional[torch.Tensor] = None, eps: float = 1e-5, out_dtype=None,
+                         want_request_output: bool = True, y_req: Optional[torch.Tensor] = None,
+                         y_cand: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         stream=None):
+    """LCB, embedding form, with the group-local norm. x_req [R, n_r, d], x_cand [C, n_c, d];
+    w_rr [k_r, n_r], w_cr [k_c, n_r], w_cc [k_c, n_c]; gamma/beta fp32 [d] or None; norm "none" |
+    "layer" | "rms". Returns (y_req [R, k_r, d] or None, y_cand [C, k_c, d]) in out_dtype (default:
+    input dtype)."""
+    lib = load_library()
+    for n, t in (("x_req", x_req), ("x_cand", x_cand), ("w_rr", w_rr), ("w_cr", w_cr), ("w_cc", w_cc),
+                 ("gamma_req", gamma_req), ("beta_req", beta_req), ("gamma_cand", gamma_cand),
+                 ("beta_cand", beta_cand)):
+        if t is not None:
+            _need_contig(n, t)
+    R, n_r, d = x_req.shape
+    C, n_c, d2 = x_cand.shape
+    k_r, k_c = w_rr.shape[0], w_cc.shape[0]
+    if d2 != d:
+        raise ValueError("x_req and x_cand must share the embedding width")
+    if w_rr.shape[1] != n_r or tuple(w_cr.shape) != (k_c, n_r) or w_cc.shape[1] != n_c:
+        raise ValueError("weight shapes do not match the embedding counts")
+    cand_to_req = _index(cand_to_req, "cand_to_req")
+    req_cand_offsets = _index(req_cand_offsets, "req_cand_offsets")
+    in_code = _dt(x_req)
+    out_code = in_code if out_dtype is None else _dt(torch.empty(0, dtype=out_dtype))
+    dev = x_cand.device
+    if y_cand is None:
+        y_cand = torch.empty((C, k_c, d), dtype=_torch_dtype(out_code), device=dev)
+    if want_request_output and y_req is None:
+        y_req = torch.empty((R, k_r, d), dtype=_torch_dtype(out_code), device=dev)
+    if not want_request_output:
+        y_req = None
+    ws = _workspace(ikbo_lcb_emb_workspace_size(R, k_c, d), dev, workspace)
+    st = lib.ikbo_lcb_emb_forward(_ptr(x_req), R, n_r, _ptr(x_cand), C, n_c, d, _ptr(w_rr), k_r, _ptr(w_cr),
+                                  _ptr(w_cc), k_c, _ptr(cand_to_req), _ptr(req_cand_offsets),
+                                  IKBO_INDEX_SORTED if sorted_index else 0, _NORMS[norm], _ptr(gamma_req),
+                                  _ptr(beta_req), _ptr(gamma_cand), _ptr(beta_cand), eps, in_code, _dt(y_cand),
+                                  _ptr(y_req), _ptr(y_cand), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream))
     _check(st)
     return y_req, y_cand
 

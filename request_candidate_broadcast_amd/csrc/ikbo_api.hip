@@ -448,6 +448,73 @@ int ikbo_fm_forward(const void *x_req, int64_t num_req, int32_t n_req_feat, cons
     return ok();
 }
 
+// ---- LCB, embedding-matrix form, with the group-local norm ----------------------------------------
+size_t ikbo_lcb_emb_workspace_size(int64_t num_req, int32_t n_cand_out, int32_t dim) {
+    if (num_req < 0 || n_cand_out < 0 || dim < 0) return 0;
+    return align256(sizeof(float) * (size_t)num_req * (size_t)n_cand_out * (size_t)dim);
+}
+
+int ikbo_lcb_emb_forward(const void *x_req, int64_t num_req, int32_t n_req_in, const void *x_cand, int64_t num_cand,
+                         int32_t n_cand_in, int32_t dim, const void *w_rr, int32_t n_req_out, const void *w_cr,
+                         const void *w_cc, int32_t n_cand_out, const int32_t *cand_to_req,
+                         const int32_t *req_cand_offsets, uint32_t index_flags, int32_t norm, const float *gamma_req,
+                         const float *beta_req, const float *gamma_cand, const float *beta_cand, float eps,
+                         int32_t in_dtype, int32_t out_dtype, void *y_req, void *y_cand, void *workspace,
+                         size_t workspace_bytes, void *hip_stream) {
+    const int64_t R = num_req, C = num_cand;
+    if (R < 0 || C < 0 || n_req_in < 1 || n_cand_in < 1 || n_req_out < 0 || n_cand_out < 0 || dim < 1)
+        return fail(IKBO_INVALID_ARGUMENT,
+                    "bad sizes (num_req %lld num_cand %lld n_req_in %d n_cand_in %d n_req_out %d n_cand_out %d dim %d)",
+                    (long long)R, (long long)C, n_req_in, n_cand_in, n_req_out, n_cand_out, dim);
+    if (dim > ikbo::kLcbeMaxDim) return fail(IKBO_UNSUPPORTED, "dim %d above %d", dim, ikbo::kLcbeMaxDim);
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(IKBO_UNSUPPORTED, "dtype in %d out %d", in_dtype, out_dtype);
+    if (norm != IKBO_NORM_NONE && norm != IKBO_NORM_LAYER && norm != IKBO_NORM_RMS)
+        return fail(IKBO_INVALID_ARGUMENT, "unknown norm %d", norm);
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(IKBO_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    int rc = check_index_args(cand_to_req, req_cand_offsets, index_flags, C);
+    if (rc) return rc;
+    const bool want_req = y_req != nullptr && R > 0 && n_req_out > 0;
+    const bool want_cand = C > 0 && n_cand_out > 0;
+    if (want_cand && (!x_cand || !y_cand || !w_cc || (R > 0 && (!w_cr || !x_req))))
+        return fail(IKBO_INVALID_ARGUMENT, "x_cand, y_cand, w_cc, w_cr and x_req must be non-NULL for the candidate group");
+    if (want_req && (!x_req || !w_rr)) return fail(IKBO_INVALID_ARGUMENT, "x_req and w_rr must be non-NULL");
+    const void *ptrs[] = {x_req, x_cand, w_rr, w_cr, w_cc, gamma_req, beta_req, gamma_cand, beta_cand, y_req, y_cand, workspace};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    const size_t need = want_cand ? ikbo_lcb_emb_workspace_size(R, n_cand_out, dim) : 0;
+    if (need && (workspace_bytes < need || !workspace))
+        return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (!want_req && !want_cand) return ok();
+    ikbo::LcbeArgs a = {};
+    a.x_r = x_req;
+    a.x_c = x_cand;
+    a.w_rr = w_rr;
+    a.w_cr = w_cr;
+    a.w_cc = w_cc;
+    a.g_r = gamma_req;
+    a.b_r = beta_req;
+    a.g_c = gamma_cand;
+    a.b_c = beta_cand;
+    a.z = want_cand && R > 0 ? (float *)workspace : nullptr;
+    a.y_r = want_req ? y_req : nullptr;
+    a.y_c = want_cand ? y_cand : nullptr;
+    a.R = R;
+    a.C = want_cand ? C : 0;
+    a.n_r = n_req_in;
+    a.n_c = n_cand_in;
+    a.k_r = n_req_out;
+    a.k_c = n_cand_out;
+    a.d = dim;
+    a.map = cand_to_req;
+    a.off = req_cand_offsets;
+    a.in_f32 = in_dtype == IKBO_F32;
+    a.out_f32 = out_dtype == IKBO_F32;
+    a.norm = norm;
+    a.eps = eps;
+    IKBO_HIP(ikbo::launch_lcbe(a, (hipStream_t)hip_stream));
+    return ok();
+}
+
 // ---- K/V projection -----------------------------------------------------------------------------
 int ikbo_kv_project(const void *s_rows, int64_t rows, int32_t d_in, const void *w_k, const void *w_v, int32_t d_out,
                     int32_t in_dtype, int32_t out_dtype, void *k_out, void *v_out, void *hip_stream) {

@@ -99,7 +99,6 @@ __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_wave_ba
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
 }
 
-// A pointer that is the same in every lane, moved to scalar registers.
 // A 64-bit value every lane holds alike, in scalar registers (branches on it are uniform)
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
@@ -107,6 +106,30 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Request of candidate c for kernels that walk candidates in increasing order: from the offsets
+// [R + 1] when given (one binary search when cursor < 0, then a linear advance from the previous
+// candidate's request), else from the map; -1 when the candidate has no valid request.
+__device__ __forceinline__ int64_t cand_request(const int32_t *off, const int32_t *map, int64_t R, int64_t c,
+                                                int64_t &cursor) {
+    if (off) {
+        if (cursor < 0) {
+            int64_t lo = 0, hi = R;          // last r with off[r] <= c
+            while (hi - lo > 1) {
+                const int64_t mid = (lo + hi) / 2;
+                if (off[mid] <= c) lo = mid;
+                else hi = mid;
+            }
+            cursor = lo;
+        }
+        while (cursor < R && off[cursor + 1] <= c) ++cursor;
+        if (cursor >= R || off[cursor] > c) return -1;
+        return cursor;
+    }
+    const int32_t r = map[c];
+    return (r >= 0 && r < R) ? r : -1;
+}
+
+// A pointer that is the same in every lane, moved to scalar registers.
 template <typename T>
 __device__ __forceinline__ T *uniform_ptr(T *p) {
     const uint64_t u = (uint64_t)p;

@@ -96,26 +96,8 @@ __device__ __forceinline__ void fm_zero(void *y, int out_f32, int64_t base, int6
     }
 }
 
-// Request of candidate c: from the offsets when given (a linear advance from the wave's previous
-// candidate, after one binary search at the start of its run), else from the map; -1 when the
-// candidate has no valid request.
 __device__ __forceinline__ int64_t fm_request(const FmArgs &a, int64_t c, int64_t &cursor) {
-    if (a.off) {
-        if (cursor < 0) {
-            int64_t lo = 0, hi = a.R;        // last r with off[r] <= c
-            while (hi - lo > 1) {
-                const int64_t mid = (lo + hi) / 2;
-                if (a.off[mid] <= c) lo = mid;
-                else hi = mid;
-            }
-            cursor = lo;
-        }
-        while (cursor < a.R && a.off[cursor + 1] <= c) ++cursor;
-        if (cursor >= a.R || a.off[cursor] > c) return -1;
-        return cursor;
-    }
-    const int32_t r = a.map[c];
-    return (r >= 0 && r < a.R) ? r : -1;
+    return cand_request(a.off, a.map, a.R, c, cursor);
 }
 
 // KS = d / 16 k steps, NB = 32-row blocks per group (1: n_r, n_c <= 32; 2: <= 64), WPE = waves per

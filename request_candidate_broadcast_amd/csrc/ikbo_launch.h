@@ -124,4 +124,24 @@ struct FmArgs {
 bool fm_mfma_supported(const FmArgs &a);
 hipError_t launch_fm(const FmArgs &a, hipStream_t s);
 
+// ---- LCB, embedding-matrix form, with the group-local norm (ikbo_lcbe.hip) -----------------------
+struct LcbeArgs {
+    const void *x_r, *x_c;              // [R, n_r, d], [C, n_c, d]
+    const void *w_rr, *w_cr, *w_cc;     // [k_r, n_r], [k_c, n_r], [k_c, n_c]
+    const float *g_r, *b_r, *g_c, *b_c; // [d] each, or null (gamma 1, beta 0)
+    float *z;                           // [R, k_c, d] fp32: W_CR X^R once per request
+    void *y_r, *y_c;                    // [R, k_r, d] or null, [C, k_c, d]
+    int64_t R, C;
+    int32_t n_r, n_c, k_r, k_c, d;
+    const int32_t *map, *off;           // candidate -> request; offsets [R + 1] take precedence when set
+    int32_t in_f32, out_f32, norm;      // norm: 0 none, 1 LayerNorm, 2 RMSNorm (per embedding row)
+    float eps;
+    int64_t chunk;                      // candidates per wave (set by launch_lcbe)
+};
+constexpr int kLcbeMaxDim = 256;
+// whether launch_lcbe takes the MFMA path for the candidates (bf16, d in {32, 64, 128},
+// n_c and k_c <= 64)
+bool lcbe_mfma_supported(const LcbeArgs &a);
+hipError_t launch_lcbe(const LcbeArgs &a, hipStream_t s);
+
 }  // namespace ikbo

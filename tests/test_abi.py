@@ -215,3 +215,39 @@ def test_fm_argument_errors(lib):
     assert fm(lib, xr=None) == ikbo.IKBO_INVALID_ARGUMENT
     assert fm(lib, yc=MIS) == ikbo.IKBO_MISALIGNED
     assert fm(lib, C=0, yr=None) == ikbo.IKBO_OK       # nothing to compute
+
+
+def lcbe(lib, **kw):
+    a = dict(xr=FAKE, R=4, nr=32, xc=FAKE, C=64, nc=32, d=64, wrr=FAKE, kr=16, wcr=FAKE, wcc=FAKE, kc=32, m=FAKE,
+             off=None, flags=0, norm=1, gr=None, br=None, gc=FAKE, bc=FAKE, eps=1e-5, ind=1, outd=1, yr=FAKE, yc=FAKE,
+             ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.ikbo_lcb_emb_forward(a["xr"], a["R"], a["nr"], a["xc"], a["C"], a["nc"], a["d"], a["wrr"], a["kr"],
+                                    a["wcr"], a["wcc"], a["kc"], a["m"], a["off"], a["flags"], a["norm"], a["gr"],
+                                    a["br"], a["gc"], a["bc"], a["eps"], a["ind"], a["outd"], a["yr"], a["yc"], a["ws"],
+                                    a["wsb"], a["stream"])
+
+
+def test_lcb_emb_argument_errors(lib):
+    # Z in fp32 [R, k_c, d]
+    assert lib.ikbo_lcb_emb_workspace_size(4, 32, 64) >= 4 * 4 * 32 * 64
+    assert lib.ikbo_lcb_emb_workspace_size(-1, 32, 64) == 0
+    assert lcbe(lib, d=0) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcbe(lib, nc=0) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcbe(lib, kc=-1) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcbe(lib, d=257) == ikbo.IKBO_UNSUPPORTED
+    assert lcbe(lib, ind=7) == ikbo.IKBO_UNSUPPORTED
+    assert lcbe(lib, norm=3) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcbe(lib, eps=-1.0) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcbe(lib, eps=float("nan")) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcbe(lib, m=None, off=None) == ikbo.IKBO_INVALID_ARGUMENT
+    assert lcbe(lib, flags=4) == ikbo.IKBO_INVALID_ARGUMENT
+    for k in ("xc", "yc", "wcc", "wcr", "xr"):
+        assert lcbe(lib, **{k: None}) == ikbo.IKBO_INVALID_ARGUMENT, k
+    assert lcbe(lib, wrr=None) == ikbo.IKBO_INVALID_ARGUMENT
+    for k in ("xr", "xc", "wrr", "wcr", "wcc", "gc", "bc", "yr", "yc", "ws"):
+        assert lcbe(lib, **{k: MIS}) == ikbo.IKBO_MISALIGNED, k
+    assert lcbe(lib, wsb=4 * 4 * 32 * 64 - 1) == ikbo.IKBO_WORKSPACE_TOO_SMALL
+    assert lcbe(lib, ws=None) == ikbo.IKBO_WORKSPACE_TOO_SMALL
+    assert lcbe(lib, C=0, yr=None) == ikbo.IKBO_OK        # nothing to compute
+    assert lcbe(lib, kc=0, yr=None, ws=None, wsb=0) == ikbo.IKBO_OK
