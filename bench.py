@@ -27,6 +27,21 @@ METRIC = "IKBO-DCA TFLOP/s + ms; IKBO-LCB ms; % of MI355X bf16 MFMA/HBM roofline
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 FM_SHAPE = (128, 2048, 32, 32, 64)   # requests, candidates per request, n_r, n_c, d
+# requests, candidates per request, n_r, n_c (input embeddings), d, k_r, k_c (output embeddings)
+LCBE_SHAPE = (128, 2048, 32, 32, 64, 32, 32)
+
+
+def lcbe_params(np, synth):
+    """Weights N(0, 1/n_in) and per-group gamma, beta of the LCB embedding-form workload."""
+    import math
+    R, per_r, n_r, n_c, d, k_r, k_c = LCBE_SHAPE
+    return dict(w_rr=synth.draw(0, 92, k_r * n_r, "bf16", 1 / math.sqrt(n_r)).reshape(k_r, n_r),
+                w_cr=synth.draw(0, 93, k_c * n_r, "bf16", 1 / math.sqrt(n_r)).reshape(k_c, n_r),
+                w_cc=synth.draw(0, 94, k_c * n_c, "bf16", 1 / math.sqrt(n_c)).reshape(k_c, n_c),
+                gamma_r=(1.0 + 0.25 * synth.draw(0, 95, d, "f32")).astype(np.float32),
+                beta_r=(0.25 * synth.draw(0, 96, d, "f32")).astype(np.float32),
+                gamma_c=(1.0 + 0.25 * synth.draw(0, 97, d, "f32")).astype(np.float32),
+                beta_c=(0.25 * synth.draw(0, 98, d, "f32")).astype(np.float32))
 
 
 def parse():
@@ -34,7 +49,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="block", choices=["block", "layer", "dca_fixed", "dca_ragged", "lcb", "fm"])
+    p.add_argument("--workload", default="block", choices=["block", "layer", "dca_fixed", "dca_ragged", "lcb", "fm", "lcb_emb"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=0, help="candidates in the oracle sample (0 = default)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -198,6 +213,35 @@ def main():
             dominant = "fm"
             config = {"workload": "GLM factorization machine (two groups, in-kernel broadcast)", "requests": R,
                       "candidates": C, "n_req_feat": n_r, "n_cand_feat": n_c, "dim": d}
+        elif args.workload == "lcb_emb":
+            # LCB embedding form (Eq. 5-6) with a per-group LayerNorm (Eq. 7) on the block's batch:
+            # 128 requests x 2048 candidates, 32 -> 32 embeddings of width 64 per group, bf16 in and out
+            R, per_r, n_r, n_c, d, k_r, k_c = LCBE_SHAPE
+            C = R * per_r
+            x_r = up(synth.draw(0, 90, R * n_r * d, "bf16").reshape(R, n_r, d))
+            x_c = up(synth.draw(0, 91, C * n_c * d, "bf16").reshape(C, n_c, d))
+            prm = {kk: up(vv) for kk, vv in lcbe_params(np, synth).items()}
+            off = up(synth.offsets_from_counts(np.full(R, per_r)))
+            y_r = torch.empty((R, k_r, d), dtype=torch.bfloat16, device=dev)
+            y_c = torch.empty((C, k_c, d), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(ikbo.ikbo_lcb_emb_workspace_size(R, k_c, d), dtype=torch.uint8, device=dev)
+            flops["lcb_emb"] = 2.0 * C * k_c * n_c * d + 2.0 * R * (k_r + k_c) * n_r * d
+            algo_bytes["lcb_emb"] = 2 * (C * n_c * d + C * k_c * d + R * n_r * d + R * k_r * d
+                                         + (k_r + k_c) * n_r + k_c * n_c) + 4 * (R + 1) + 4 * 4 * d
+
+            def step(ev):
+                ev[0].record(stream)
+                ikbo.ikbo_lcb_emb_forward(x_r, x_c, prm["w_rr"], prm["w_cr"], prm["w_cc"], req_cand_offsets=off,
+                                          norm="layer", gamma_req=prm["gamma_r"], beta_req=prm["beta_r"],
+                                          gamma_cand=prm["gamma_c"], beta_cand=prm["beta_c"], y_req=y_r, y_cand=y_c,
+                                          workspace=ws, stream=stream)
+                ev[1].record(stream)
+
+            names = [("lcb_emb", 0, 1)]
+            dominant = "lcb_emb"
+            config = {"workload": "LCB embedding form + group-local LayerNorm (two groups, in-kernel broadcast)",
+                      "requests": R, "candidates": C, "n_req_in": n_r, "n_cand_in": n_c, "dim": d,
+                      "n_req_out": k_r, "n_cand_out": k_c, "norm": "layer"}
         elif args.workload in ("dca_fixed", "dca_ragged"):
             s = synth.dca_spec(args.workload)
             q = up(synth.dca_q(s))
@@ -300,7 +344,7 @@ def main():
                 traffic = ent.get("bytes_per_launch")
     except (OSError, ValueError, KeyError):
         traffic = None
-    if dominant == "fm":      # HBM-bound (about 32 FLOP per byte at bf16 in and out)
+    if dominant in ("fm", "lcb_emb"):      # HBM-bound (16-32 FLOP per byte at bf16 in and out)
         gbs = dk["gbs_algorithmic"]
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dominant,
@@ -400,6 +444,23 @@ def cpu_baseline(args, np):
         oracle.fm(x_r, x_c, m=m_sub)
         secs = time.perf_counter() - t0
         work = 2.0 * len(m_sub) * n_c * (n_r + n_c) * d
+        sample = "%d candidates (the first %d of each of the %d requests)" % (len(m_sub), n_per, len(reqs))
+    elif args.workload == "lcb_emb":
+        R, per_r, n_r, n_c, d, k_r, k_c = LCBE_SHAPE
+        # every request and all their candidates: the whole workload (a few seconds of oracle work)
+        reqs = list(range(R))
+        n_per = min(per_r, args.cpu_sample // len(reqs)) if args.cpu_sample else per_r
+        x_r = synth.draw(0, 90, R * n_r * d, "bf16").reshape(R, n_r, d)
+        x_c = np.concatenate([synth.draw(0, 91, n_per * n_c * d, "bf16", start=r * per_r * n_c * d)
+                              for r in reqs]).reshape(-1, n_c, d)
+        m_sub = np.repeat(np.array(reqs, np.int32), n_per)
+        prm = lcbe_params(np, synth)
+        t0 = time.perf_counter()
+        oracle.lcb_emb(x_r, x_c, prm["w_rr"], prm["w_cr"], prm["w_cc"], m=m_sub, norm="layer",
+                       gamma_r=prm["gamma_r"], beta_r=prm["beta_r"], gamma_c=prm["gamma_c"], beta_c=prm["beta_c"],
+                       want_request=True)
+        secs = time.perf_counter() - t0
+        work = 2.0 * len(m_sub) * k_c * n_c * d + 2.0 * R * (k_r + k_c) * n_r * d
         sample = "%d candidates (the first %d of each of the %d requests)" % (len(m_sub), n_per, len(reqs))
     elif args.workload in ("dca_fixed", "dca_ragged"):
         s = synth.dca_spec(args.workload)

@@ -32,9 +32,11 @@ namespace {
 
 constexpr int kLeWaves = 4;            // waves per workgroup (every kernel here)
 
-__device__ __forceinline__ float le_in(const void *p, int in_f32, int64_t i) {
-    if (in_f32) return ((const float *)p)[i];
-    return __uint_as_float((uint32_t)((const uint16_t *)p)[i] << 16);
+// One input element; the dtype is a template parameter so no load sits behind a branch.
+template <bool F32>
+__device__ __forceinline__ float le_in(const void *p, int64_t i) {
+    if constexpr (F32) return ((const float *)p)[i];
+    else return __uint_as_float((uint32_t)((const uint16_t *)p)[i] << 16);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -92,6 +94,7 @@ __device__ __forceinline__ void store_out(void *y, int out_f32, int64_t i, float
 
 // Request side: per request r, rows [0, kr) are Y^R (= W_RR X^R_r, normalised) and rows
 // [kr, kr + kc) are Z_r = W_CR X^R_r (fp32, no norm); kr = 0 without y_r, kc = 0 without z.
+template <bool F32>
 __global__ __launch_bounds__(kLeWaves * 64) void lcbe_request_kernel(LcbeArgs a) {
     constexpr int T = kLcbeMaxDim / 64;
     const int lane = threadIdx.x & 63;
@@ -109,10 +112,12 @@ __global__ __launch_bounds__(kLeWaves * 64) void lcbe_request_kernel(LcbeArgs a)
         for (int t = 0; t < T; ++t) {
             const int j = lane + 64 * t;
             float s = 0.0f;
+            // unrolled so the loads of eight k are in flight together (the sum stays in k order)
             if (j < a.d)
+#pragma unroll 8
                 for (int k = 0; k < a.n_r; ++k)
-                    s = __builtin_fmaf(le_in(wsrc, a.in_f32, (int64_t)orow * a.n_r + k),
-                                       le_in(a.x_r, a.in_f32, (r * a.n_r + k) * a.d + j), s);
+                    s = __builtin_fmaf(le_in<F32>(wsrc, (int64_t)orow * a.n_r + k),
+                                       le_in<F32>(a.x_r, (r * a.n_r + k) * a.d + j), s);
             v[t] = s;
         }
         if (!is_y) {
@@ -129,6 +134,7 @@ __global__ __launch_bounds__(kLeWaves * 64) void lcbe_request_kernel(LcbeArgs a)
 }
 
 // Candidates, any shape and dtype: one wave per output row (c, o).
+template <bool F32>
 __global__ __launch_bounds__(kLeWaves * 64) void lcbe_cand_generic_kernel(LcbeArgs a) {
     constexpr int T = kLcbeMaxDim / 64;
     const int lane = threadIdx.x & 63;
@@ -145,9 +151,10 @@ __global__ __launch_bounds__(kLeWaves * 64) void lcbe_cand_generic_kernel(LcbeAr
             const int j = lane + 64 * t;
             float s = 0.0f;
             if (j < a.d && r >= 0) {
+#pragma unroll 8
                 for (int k = 0; k < a.n_c; ++k)
-                    s = __builtin_fmaf(le_in(a.w_cc, a.in_f32, (int64_t)o * a.n_c + k),
-                                       le_in(a.x_c, a.in_f32, (c * a.n_c + k) * a.d + j), s);
+                    s = __builtin_fmaf(le_in<F32>(a.w_cc, (int64_t)o * a.n_c + k),
+                                       le_in<F32>(a.x_c, (c * a.n_c + k) * a.d + j), s);
                 s += a.z[(r * a.k_c + o) * a.d + j];
             }
             v[t] = s;
@@ -255,12 +262,6 @@ __global__ __launch_bounds__(kLeWaves * 64) __attribute__((amdgpu_waves_per_eu(W
     float4 zf[ZCACHE ? OB : 1][ZCACHE ? JB : 1][4];
     int64_t have_r = -1, cursor = -1;
     const int q8 = lane % C8, r8 = lane / C8;
-    float gg[8], bb[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        gg[t] = a.norm ? gb[0][8 * q8 + t] : 1.0f;
-        bb[t] = a.norm ? gb[1][8 * q8 + t] : 0.0f;
-    }
     if (PREFETCH) fetch(c0);
     for (int64_t c = c0; c < c1; ++c) {
         const int64_t r = uniform64(cand_request(a.off, a.map, a.R, c, cursor));
@@ -363,6 +364,16 @@ __global__ __launch_bounds__(kLeWaves * 64) __attribute__((amdgpu_waves_per_eu(W
             wave_lds_fence();
             // whole rows out: lane takes columns 8 q8 .. 8 q8 + 7 of rows r8, r8 + RPI, ...
             const int nrows = min(32, a.k_c - 32 * ob);
+            // gamma and beta of the lane's columns, read here rather than held across the loop:
+            // the offset is an opaque zero, so the compiler cannot hoist these reads out of it
+            int zero;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+            float gg[8], bb[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                gg[t] = a.norm ? gb[0][8 * q8 + t + zero] : 1.0f;
+                bb[t] = a.norm ? gb[1][8 * q8 + t + zero] : 0.0f;
+            }
 #pragma unroll
             for (int it = 0; it < 32 / RPI; ++it) {
                 const int row = it * RPI + r8;
@@ -405,7 +416,8 @@ hipError_t launch_lcbe(const LcbeArgs &a0, hipStream_t s) {
     if (rrows > 0) {
         int64_t grid = (rrows + kLeWaves - 1) / kLeWaves;
         if (grid > 65536) grid = 65536;
-        hipLaunchKernelGGL(lcbe_request_kernel, dim3((unsigned)grid), dim3(kLeWaves * 64), 0, s, a);
+        if (a.in_f32) hipLaunchKernelGGL(lcbe_request_kernel<true>, dim3((unsigned)grid), dim3(kLeWaves * 64), 0, s, a);
+        else hipLaunchKernelGGL(lcbe_request_kernel<false>, dim3((unsigned)grid), dim3(kLeWaves * 64), 0, s, a);
     }
     if (a.C > 0 && a.k_c > 0) {
         if (lcbe_mfma_supported(a)) {
@@ -434,7 +446,10 @@ hipError_t launch_lcbe(const LcbeArgs &a0, hipStream_t s) {
         } else {
             int64_t grid = (a.C * a.k_c + kLeWaves - 1) / kLeWaves;
             if (grid > 65536) grid = 65536;
-            hipLaunchKernelGGL(lcbe_cand_generic_kernel, dim3((unsigned)grid), dim3(kLeWaves * 64), 0, s, a);
+            if (a.in_f32)
+                hipLaunchKernelGGL(lcbe_cand_generic_kernel<true>, dim3((unsigned)grid), dim3(kLeWaves * 64), 0, s, a);
+            else
+                hipLaunchKernelGGL(lcbe_cand_generic_kernel<false>, dim3((unsigned)grid), dim3(kLeWaves * 64), 0, s, a);
         }
     }
     return hipGetLastError();
