@@ -20,6 +20,10 @@ then evaluates the definitions:
 * ``fm``    the GLM factorization machine, Sec. 3.1.4 Eq. 9-10 (two groups): request outputs
             X^R (X^R)^T, candidate outputs [X^C (X^R_m)^T, X^C (X^C)^T], in fp64 with the request
             rows expanded per candidate.
+* ``dca_layer`` one DCA interaction layer, Sec. 3.2 Eq. 12-13: the query generator (``glm``), the
+            K/V projections of the layer's sequence rows for both halves (``linear``), A^C
+            (``dca``) and A^R (``request_attention``), each group's output the concatenation
+            [Q | A] that the next layer reads; composed in fp64 with no rounding in between.
 * ``lcb_emb`` the ROCSified LCB in its embedding-matrix (row-axis) form, Sec. 3.1.2 Eq. 5-6 (two
             groups): Y^R = W_RR X^R, Y^C = W_CR X^R_m + W_CC X^C, followed by the group-local
             normalisation of Sec. 3.1.3 Eq. 7 (LayerNorm or RMSNorm of each embedding row), in
@@ -126,13 +130,13 @@ def dca(q: np.ndarray, k: np.ndarray, v: np.ndarray, R: int, *, m=None, off=None
     """Cross attention of candidate queries over their request's K/V, fp64.
 
     q [C, Lq, H, d]; k, v [R, L, H, d] or varlen [sum L_r, H, d] with kv_cu [R+1].
-    q may also be float64 (a chained fp64 query). Returns [n, Lq, H, d] fp64 for the candidates
-    `cands` (all when None)."""
+    q, k and v may also be float64 (chained fp64 values). Returns [n, Lq, H, d] fp64 for the
+    candidates `cands` (all when None)."""
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
     v = np.ascontiguousarray(v)
-    dt = _dtype_code(k)
-    assert _dtype_code(v) == dt
+    dt = F64 if k.dtype == np.float64 else _dtype_code(k)
+    assert (F64 if v.dtype == np.float64 else _dtype_code(v)) == dt
     qdt = F64 if q.dtype == np.float64 else _dtype_code(q)
     C, Lq, H, d = q.shape
     m, off, kv_cu = _i32(m), _i32(off), _i32(kv_cu)
@@ -256,6 +260,34 @@ def fm(x_r: np.ndarray, x_c: np.ndarray, *, m=None, off=None, cands: Optional[Se
     if want_request:
         out["y_r"] = np.stack([xr[r] @ xr[r].T for r in range(R)]) if R else np.zeros((0, n_r, n_r))
     return out
+
+
+def dca_layer(x_r: np.ndarray, x_c: np.ndarray, glm_layers: Sequence[dict], seq: np.ndarray, w_kc: np.ndarray,
+              w_vc: np.ndarray, w_kr: np.ndarray, w_vr: np.ndarray, *, q_len: int, heads: int, m=None, off=None,
+              kv_cu=None, scale: Optional[float] = None, cands: Optional[Sequence[int]] = None,
+              nthreads: Optional[int] = None):
+    """One DCA interaction layer (Eq. 12-13): y = [Q | A] per group, fp64.
+
+    x_r [R, k_r], x_c [C, k_c], seq [rows, seq_dim] (R * L rows, or sum L_r with kv_cu), the
+    glm layers' last widths W = q_len * heads * d, K/V weights [heads * d, seq_dim]. Returns
+    {"y_c": [n, 2W]} for the candidates `cands` (all when None) and "y_r": [R, 2W]."""
+    R = x_r.shape[0]
+    g = glm(x_r, x_c, glm_layers, m=m, off=off, cands=cands, want_request=True, nthreads=nthreads)
+    W = g["y_c"].shape[1]
+    d = W // (q_len * heads)
+    rows = seq.shape[0]
+    kv_shape = (R, rows // R, heads, d) if kv_cu is None and R > 0 else (rows, heads, d)
+    kc, vc = linear(seq, w_kc).reshape(kv_shape), linear(seq, w_vc).reshape(kv_shape)
+    kr, vr = linear(seq, w_kr).reshape(kv_shape), linear(seq, w_vr).reshape(kv_shape)
+    C = x_c.shape[0]
+    ids = np.arange(C) if cands is None else np.asarray(cands, dtype=np.int64)
+    # the candidates' requests, then A^C of exactly those query rows
+    req = np.array([request_of(m, off, R, int(c)) for c in ids], dtype=np.int32)
+    q_c = g["y_c"].reshape(len(ids), q_len, heads, d)
+    a_c = dca(q_c, kc, vc, R, m=req, kv_cu=kv_cu, scale=scale, nthreads=nthreads).reshape(len(ids), W)
+    q_r = g["y_r"].reshape(R, q_len, heads, d)
+    a_r = request_attention(q_r, kr, vr, kv_cu=kv_cu, scale=scale, nthreads=nthreads).reshape(R, W)
+    return {"y_c": np.concatenate([g["y_c"], a_c], axis=1), "y_r": np.concatenate([g["y_r"], a_r], axis=1)}
 
 
 NORM = {"none": 0, "layer": 1, "rms": 2}

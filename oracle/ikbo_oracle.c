@@ -198,7 +198,7 @@ int oracle_dca(const void *q, int64_t C, int Lq, const void *k, const void *v, i
                int64_t *violations, int nthreads) {
     if (!q || !k || !v || !out || (!m && !off) || C < 0 || R < 0 || Lq <= 0 || H <= 0 || d <= 0 || L < 0)
         return OR_BAD_ARG;
-    if (dtype != OR_F32 && dtype != OR_BF16) return OR_BAD_ARG;
+    if (dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_F64) return OR_BAD_ARG;
     if (qdtype != OR_F32 && qdtype != OR_BF16 && qdtype != OR_F64) return OR_BAD_ARG;
     if (!cands) n = C;
     if (kv_cu)
