@@ -232,6 +232,46 @@ int ikbo_fm_forward(const void *x_req, int64_t num_req, int32_t n_req_feat,
                     int32_t in_dtype, int32_t out_dtype, void *y_req, void *y_cand, void *hip_stream);
 
 /* ------------------------------------------------------------------------------------------
+ * One DCA interaction layer (Sec. 3.2: the query generator of Eq. 12, the two attention halves
+ * of Eq. 13, and the concatenation of each attention output with its group's GLM
+ * representation that feeds the next layer; stacking layers is "Benefiting from Depth"):
+ *   [Q^R | Q^C] = GLM-MLP(x_req, x_cand)               (the glm_layers, as ikbo_glm_mlp_forward)
+ *   K^C, V^C = S W_K^C, S W_V^C;  K^R, V^R = S W_K^R, S W_V^R   (once per request, as ikbo_kv_project)
+ *   A^C = IKBO-DCA(Q^C, K^C, V^C) (as ikbo_dca_forward);  A^R = Attn(Q^R, K^R, V^R) (as
+ *         ikbo_request_attention)
+ *   y_req = [Q^R | A^R]  [num_req, 2 W],   y_cand = [Q^C | A^C]  [num_cand, 2 W],   W = q_len *
+ *         num_heads * head_dim (each row: the W query values viewed [q_len, num_heads, head_dim],
+ *         then the W attention outputs in the same layout).
+ * The halves are written in place (strided), so the next layer reads y_req / y_cand as its
+ * x_req / x_cand with k_req = k_cand = 2 W. S is this layer's request sequence representation
+ * (the shared encoder that produces it is request-only and not part of this call).
+ * x_req, x_cand, cand_to_req, req_cand_offsets, index_flags, glm_layers: as ikbo_glm_mlp_forward;
+ *        the last glm layer must output W columns per group.
+ * seq    [seq_rows, seq_dim] (dtype): R * kv_len rows for a uniform length, sum L_r rows with
+ *        kv_cu_seqlens (seq_rows must then equal kv_cu_seqlens[num_req]).
+ * w_k_cand, w_v_cand, w_k_req, w_v_req  [num_heads * head_dim, seq_dim] (dtype).
+ * q_len, num_heads, head_dim, softmax_scale: as ikbo_dca_forward.
+ * dtype  IKBO_BF16 or IKBO_F32 for inputs, weights, intermediates and outputs (fp32 accumulation).
+ * workspace >= ikbo_dca_layer_workspace_size(...) bytes (the MLP's, two K/V buffers reused by both
+ *        halves, and the attention's).
+ * Errors: those of the calls above, plus IKBO_INVALID_ARGUMENT for a query generator whose output
+ *         width is not W or a seq_rows that does not match.
+ * ---------------------------------------------------------------------------------------- */
+size_t ikbo_dca_layer_workspace_size(int64_t num_cand, int64_t num_req, int32_t num_glm_layers,
+                                     const ikbo_glm_layer *glm_layers, int64_t seq_rows, int32_t num_heads,
+                                     int32_t head_dim, int32_t dtype);
+
+int ikbo_dca_layer_forward(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
+                           const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                           int32_t num_glm_layers, const ikbo_glm_layer *glm_layers,
+                           const void *seq, int64_t seq_rows, int32_t seq_dim,
+                           const int32_t *kv_cu_seqlens, int32_t kv_len,
+                           const void *w_k_cand, const void *w_v_cand, const void *w_k_req, const void *w_v_req,
+                           int32_t q_len, int32_t num_heads, int32_t head_dim, float softmax_scale,
+                           int32_t dtype, void *y_req, void *y_cand, void *workspace,
+                           size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------------------------------------
  * LCB in its embedding-matrix (row-axis) form, two groups (Sec. 3.1.2, Eq. 5 and the block
  * form Eq. 6), each group's output then normalised on its own (Sec. 3.1.3, Eq. 7):
  *   y_req[r]  = Norm_R( W_RR X^R_r )                                   [n_req_out, dim]

@@ -57,7 +57,8 @@ EXPORTS = ["ikbo_version", "ikbo_status_string", "ikbo_last_error_message",
            "ikbo_lcb_workspace_size", "ikbo_lcb_forward",
            "ikbo_glm_mlp_workspace_size", "ikbo_glm_mlp_forward", "ikbo_check_index",
            "ikbo_kv_project", "ikbo_request_attention_workspace_size", "ikbo_request_attention",
-           "ikbo_fm_forward", "ikbo_lcb_emb_workspace_size", "ikbo_lcb_emb_forward"]
+           "ikbo_fm_forward", "ikbo_lcb_emb_workspace_size", "ikbo_lcb_emb_forward",
+           "ikbo_dca_layer_workspace_size", "ikbo_dca_layer_forward"]
 
 _lib = None
 
@@ -107,6 +108,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ikbo_lcb_emb_forward.restype = ctypes.c_int
     lib.ikbo_lcb_emb_forward.argtypes = [vp, i64, i32, vp, i64, i32, i32, vp, i32, vp, vp, i32, vp, vp, u32, i32,
                                          vp, vp, vp, vp, f32, i32, i32, vp, vp, vp, sz, vp]
+    lib.ikbo_dca_layer_workspace_size.restype = sz
+    lib.ikbo_dca_layer_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(GlmLayer), i64, i32, i32, i32]
+    lib.ikbo_dca_layer_forward.restype = ctypes.c_int
+    lib.ikbo_dca_layer_forward.argtypes = [vp, i64, vp, i64, vp, vp, u32, i32, ctypes.POINTER(GlmLayer), vp, i64, i32,
+                                           vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
     lib.ikbo_request_attention.restype = ctypes.c_int
     lib.ikbo_request_attention.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, i32, f32, i32, i32, vp, vp, sz, vp]
     _lib = lib
@@ -449,6 +455,48 @@ def ikbo_glm_mlp_forward(x_req: torch.Tensor, x_cand: torch.Tensor, layers: Sequ
                                   IKBO_INDEX_SORTED if sorted_index else 0, len(layers), arr, in_code, out_code,
                                   _ptr(y_req), _ptr(y_cand), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(stream))
+    _check(st)
+    return y_req, y_cand
+
+
+def ikbo_dca_layer_forward(x_req: torch.Tensor, x_cand: torch.Tensor, glm_layers: Sequence[dict], seq: torch.Tensor,
+                           w_k_cand: torch.Tensor, w_v_cand: torch.Tensor, w_k_req: torch.Tensor,
+                           w_v_req: torch.Tensor, *, q_len: int, num_heads: int, head_dim: int,
+                           cand_to_req: Optional[torch.Tensor] = None, req_cand_offsets: Optional[torch.Tensor] = None,
+                           sorted_index: bool = False, kv_cu_seqlens: Optional[torch.Tensor] = None,
+                           kv_len: Optional[int] = None, softmax_scale: float = 0.0,
+                           y_req: Optional[torch.Tensor] = None, y_cand: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """One DCA interaction layer: y = [Q | A] per group (W = q_len * num_heads * head_dim columns each).
+    x_req [R, k_req], x_cand [C, k_cand]; seq [rows, seq_dim] (R * kv_len rows, or sum L_r with
+    kv_cu_seqlens); K/V weights [num_heads * head_dim, seq_dim]. Returns (y_req [R, 2W], y_cand [C, 2W])."""
+    lib = load_library()
+    for n, t in (("x_req", x_req), ("x_cand", x_cand), ("seq", seq), ("w_k_cand", w_k_cand), ("w_v_cand", w_v_cand),
+                 ("w_k_req", w_k_req), ("w_v_req", w_v_req)):
+        _need_contig(n, t)
+    R, C = x_req.shape[0], x_cand.shape[0]
+    rows, seq_dim = seq.shape
+    cand_to_req = _index(cand_to_req, "cand_to_req")
+    req_cand_offsets = _index(req_cand_offsets, "req_cand_offsets")
+    kv_cu_seqlens = _index(kv_cu_seqlens, "kv_cu_seqlens")
+    if kv_cu_seqlens is None and kv_len is None:
+        kv_len = rows // max(R, 1)
+    code = _dt(x_req)
+    arr = _layer_structs(glm_layers)
+    W = q_len * num_heads * head_dim
+    dev = x_cand.device
+    if y_cand is None:
+        y_cand = torch.empty((C, 2 * W), dtype=_torch_dtype(code), device=dev)
+    if y_req is None:
+        y_req = torch.empty((R, 2 * W), dtype=_torch_dtype(code), device=dev)
+    nbytes = int(lib.ikbo_dca_layer_workspace_size(C, R, len(glm_layers), arr, rows, num_heads, head_dim, code))
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib.ikbo_dca_layer_forward(_ptr(x_req), R, _ptr(x_cand), C, _ptr(cand_to_req), _ptr(req_cand_offsets),
+                                    IKBO_INDEX_SORTED if sorted_index else 0, len(glm_layers), arr, _ptr(seq), rows,
+                                    seq_dim, _ptr(kv_cu_seqlens), 0 if kv_len is None else kv_len, _ptr(w_k_cand),
+                                    _ptr(w_v_cand), _ptr(w_k_req), _ptr(w_v_req), q_len, num_heads, head_dim,
+                                    softmax_scale, code, _ptr(y_req), _ptr(y_cand), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream))
     _check(st)
     return y_req, y_cand
 

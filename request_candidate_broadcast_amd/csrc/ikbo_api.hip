@@ -129,7 +129,7 @@ size_t lcb_ws(int64_t C, int64_t R, int32_t k_req, int32_t n_req, int32_t n_cand
 int run_lcb(const void *x_req, int64_t R, int32_t k_req, const void *x_cand, int64_t C, int32_t k_cand,
             const int32_t *map, const void *w_rr, const void *w_cr, const void *w_cc, const float *b_r,
             const float *b_c, int32_t n_req, int32_t n_cand, int32_t act, int32_t in_dtype, int32_t out_dtype,
-            void *y_req, void *y_cand, const LcbWs &ws, hipStream_t s) {
+            void *y_req, void *y_cand, int64_t ldo_r, int64_t ldo_c, const LcbWs &ws, hipStream_t s) {
     const int in_f32 = in_dtype == IKBO_F32;
     const bool want_req = y_req != nullptr && n_req > 0;
     // bf16 with both GEMMs on direct copies, IKBO_LCB_FUSED=1: one persistent launch that
@@ -137,7 +137,7 @@ int run_lcb(const void *x_req, int64_t R, int32_t k_req, const void *x_cand, int
     // two launches below bit for bit; on this part the two launches are faster (the split-K
     // request GEMM already fills the GPU for its few microseconds, and the persistent loop adds a
     // claim and a flag check per tile), so they are the default.
-    if (R > 0 && C > 0 && n_cand > 0 && !in_f32 && getenv_flag("IKBO_LCB_FUSED")) {
+    if (R > 0 && C > 0 && n_cand > 0 && !in_f32 && ldo_r == n_req && ldo_c == n_cand && getenv_flag("IKBO_LCB_FUSED")) {
         ikbo::LcbFusedArgs f = {};
         ikbo::GemmArgs &g = f.req;
         g.x = x_req;
@@ -203,7 +203,7 @@ int run_lcb(const void *x_req, int64_t R, int32_t k_req, const void *x_cand, int
             return fail(IKBO_WORKSPACE_TOO_SMALL, "internal: request GEMM partials exceed the workspace sizing");
         IKBO_HIP(ikbo::launch_gemm(g, s));
         IKBO_HIP(ikbo::launch_splitk_reduce(ws.partial, g.splits, R, g.N, want_req ? n_req : 0, b_r, act, y_req,
-                                            out_dtype == IKBO_F32, ws.z, s));
+                                            out_dtype == IKBO_F32, ldo_r, ws.z, s));
     }
     // candidate GEMM with the broadcast-add fused in the epilogue (Sec. 4.2.1, Eq. 14)
     if (C > 0 && n_cand > 0) {
@@ -223,7 +223,7 @@ int run_lcb(const void *x_req, int64_t R, int32_t k_req, const void *x_cand, int
         g.map = map;
         g.R = R;
         g.out = y_cand;
-        g.ldo = n_cand;
+        g.ldo = ldo_c;
         g.out_f32 = out_dtype == IKBO_F32;
         g.act = act;
         g.partial = nullptr;
@@ -310,13 +310,18 @@ static int dca_validate(const void *q, int64_t C, int32_t q_len, const void *k, 
 }
 
 // The DCA launches of ikbo_dca_forward, arguments already validated
+// q_cs / o_cs: elements from one candidate's query (output) rows to the next's; 0 means packed
+// (q_len * num_heads * head_dim).
 static int dca_run(const void *q, int64_t C, int32_t q_len, const void *k, const void *v, int64_t R,
                    const int32_t *kv_cu_seqlens, int32_t kv_len, const int32_t *cand_to_req,
                    const int32_t *req_cand_offsets, int32_t num_heads, int32_t head_dim, float softmax_scale,
-                   int32_t in_dtype, int32_t out_dtype, void *out, void *workspace, hipStream_t s) {
+                   int32_t in_dtype, int32_t out_dtype, void *out, void *workspace, hipStream_t s, int64_t q_cs = 0,
+                   int64_t o_cs = 0) {
     if (C == 0) return ok();
     const int in_f32 = in_dtype == IKBO_F32;
     const int64_t row_elems = (int64_t)q_len * num_heads * head_dim;
+    if (q_cs == 0) q_cs = row_elems;
+    if (o_cs == 0) o_cs = row_elems;
     const int ob = (int)esize(out_dtype);
     // few stacked query rows per request (at most 32 on average): one-wave, 32-row work tiles
     const int small = !in_f32 && C * (int64_t)q_len <= 32 * R;
@@ -328,13 +333,13 @@ static int dca_run(const void *q, int64_t C, int32_t q_len, const void *k, const
     const int32_t *perm_used = nullptr;
     if (req_cand_offsets) {
         IKBO_HIP(ikbo::launch_scan_tiles(nullptr, req_cand_offsets, R, C, q_len, num_heads, bm, off, nullptr, tiles, s));
-        IKBO_HIP(ikbo::launch_zero_uncovered(req_cand_offsets, R, C, out, row_elems, ob, s));
+        IKBO_HIP(ikbo::launch_zero_uncovered(req_cand_offsets, R, C, out, row_elems, o_cs, ob, s));
     } else {
         // group an arbitrary map: histogram -> scan -> scatter (the scan leaves the cursor in counts)
         IKBO_HIP(ikbo::launch_fill_i32(counts, R + 1, 0, s));
         IKBO_HIP(ikbo::launch_histogram(cand_to_req, C, R, counts, s));
         IKBO_HIP(ikbo::launch_scan_tiles(counts, nullptr, R, C, q_len, num_heads, bm, off, counts, tiles, s));
-        IKBO_HIP(ikbo::launch_scatter(cand_to_req, C, R, counts, perm, out, row_elems, ob, s));
+        IKBO_HIP(ikbo::launch_scatter(cand_to_req, C, R, counts, perm, out, row_elems, o_cs, ob, s));
         perm_used = perm;
     }
     if (R == 0) return ok();
@@ -358,6 +363,8 @@ static int dca_run(const void *q, int64_t C, int32_t q_len, const void *k, const
     a.in_f32 = in_f32;
     a.out_f32 = out_dtype == IKBO_F32;
     a.small = small;
+    a.q_cs = q_cs;
+    a.o_cs = o_cs;
     IKBO_HIP(ikbo::launch_dca(a, s));
     return ok();
 }
@@ -380,10 +387,11 @@ size_t ikbo_request_attention_workspace_size(int64_t num_req) {
     return align256(sizeof(int32_t) * (size_t)(num_req + 1)) + ikbo_dca_workspace_size(num_req, num_req);
 }
 
-int ikbo_request_attention(const void *q_req, int64_t num_req, int32_t q_len, const void *k, const void *v,
-                           const int32_t *kv_cu_seqlens, int32_t kv_len, int32_t num_heads, int32_t head_dim,
-                           float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out, void *workspace,
-                           size_t workspace_bytes, void *hip_stream) {
+// q_cs / o_cs: elements between consecutive requests' query (output) rows; 0 means packed.
+static int request_attention_impl(const void *q_req, int64_t num_req, int32_t q_len, const void *k, const void *v,
+                                  const int32_t *kv_cu_seqlens, int32_t kv_len, int32_t num_heads, int32_t head_dim,
+                                  float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream, int64_t q_cs, int64_t o_cs) {
     const int64_t R = num_req;
     if (R < 0) return fail(IKBO_INVALID_ARGUMENT, "negative num_req");
     const size_t need = ikbo_request_attention_workspace_size(R);
@@ -402,7 +410,15 @@ int ikbo_request_attention(const void *q_req, int64_t num_req, int32_t q_len, co
     hipStream_t s = (hipStream_t)hip_stream;
     IKBO_HIP(ikbo::launch_iota_i32(ident, R + 1, s));
     return dca_run(q_req, R, q_len, k, v, R, kv_cu_seqlens, kv_len, nullptr, ident, num_heads, head_dim, softmax_scale,
-                   in_dtype, out_dtype, out, rest, s);
+                   in_dtype, out_dtype, out, rest, s, q_cs, o_cs);
+}
+
+int ikbo_request_attention(const void *q_req, int64_t num_req, int32_t q_len, const void *k, const void *v,
+                           const int32_t *kv_cu_seqlens, int32_t kv_len, int32_t num_heads, int32_t head_dim,
+                           float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out, void *workspace,
+                           size_t workspace_bytes, void *hip_stream) {
+    return request_attention_impl(q_req, num_req, q_len, k, v, kv_cu_seqlens, kv_len, num_heads, head_dim,
+                                  softmax_scale, in_dtype, out_dtype, out, workspace, workspace_bytes, hip_stream, 0, 0);
 }
 
 // ---- GLM factorization machine -------------------------------------------------------------------
@@ -588,7 +604,7 @@ int ikbo_lcb_forward(const void *x_req, int64_t num_req, int32_t k_req, const vo
         map = ws.map;
     }
     rc = run_lcb(x_req, R, k_req, x_cand, C, k_cand, map, w_rr, w_cr, w_cc, b_r, b_c, n_req_out, n_cand_out, activation,
-                 in_dtype, out_dtype, y_req, y_cand, ws, s);
+                 in_dtype, out_dtype, y_req, y_cand, n_req_out, n_cand_out, ws, s);
     return rc ? rc : ok();
 }
 
@@ -624,10 +640,12 @@ size_t ikbo_glm_mlp_workspace_size(int64_t num_cand, int64_t num_req, int32_t nu
     return cv.used;
 }
 
-int ikbo_glm_mlp_forward(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
-                         const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
-                         int32_t num_layers, const ikbo_glm_layer *layers, int32_t in_dtype, int32_t out_dtype,
-                         void *y_req, void *y_cand, void *workspace, size_t workspace_bytes, void *hip_stream) {
+// The GLM-MLP with the last layer's outputs written with row strides ldo_r / ldo_c (0: packed).
+static int glm_mlp_impl(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
+                        const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                        int32_t num_layers, const ikbo_glm_layer *layers, int32_t in_dtype, int32_t out_dtype,
+                        void *y_req, void *y_cand, int64_t ldo_r, int64_t ldo_c, void *workspace,
+                        size_t workspace_bytes, void *hip_stream) {
     const int64_t C = num_cand, R = num_req;
     if (C < 0 || R < 0) return fail(IKBO_INVALID_ARGUMENT, "negative num_cand / num_req");
     if (num_layers <= 0 || !layers) return fail(IKBO_INVALID_ARGUMENT, "need num_layers >= 1 and a host layer array");
@@ -696,13 +714,104 @@ int ikbo_glm_mlp_forward(const void *x_req, int64_t num_req, const void *x_cand,
         const bool is_last = l + 1 == num_layers;
         void *yr = is_last ? y_req : hr[l & 1];
         void *yc = is_last ? y_cand : hc[l & 1];
+        const int64_t lr = is_last && ldo_r ? ldo_r : ly.n_req_out, lc = is_last && ldo_c ? ldo_c : ly.n_cand_out;
         rc = run_lcb(xr, R, ly.k_req, xc, C, ly.k_cand, map, ly.w_rr, ly.w_cr, ly.w_cc, ly.b_r, ly.b_c, ly.n_req_out,
-                     ly.n_cand_out, ly.activation, in_dtype, is_last ? out_dtype : in_dtype, yr, yc, ws, s);
+                     ly.n_cand_out, ly.activation, in_dtype, is_last ? out_dtype : in_dtype, yr, yc, lr, lc, ws, s);
         if (rc) return rc;
         xr = yr;
         xc = yc;
     }
     return ok();
+}
+
+int ikbo_glm_mlp_forward(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
+                         const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                         int32_t num_layers, const ikbo_glm_layer *layers, int32_t in_dtype, int32_t out_dtype,
+                         void *y_req, void *y_cand, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    return glm_mlp_impl(x_req, num_req, x_cand, num_cand, cand_to_req, req_cand_offsets, index_flags, num_layers, layers,
+                        in_dtype, out_dtype, y_req, y_cand, 0, 0, workspace, workspace_bytes, hip_stream);
+}
+
+// ---- one DCA interaction layer ------------------------------------------------------------------
+size_t ikbo_dca_layer_workspace_size(int64_t num_cand, int64_t num_req, int32_t num_glm_layers,
+                                     const ikbo_glm_layer *glm_layers, int64_t seq_rows, int32_t num_heads,
+                                     int32_t head_dim, int32_t dtype) {
+    if (num_cand < 0 || num_req < 0 || seq_rows < 0 || num_heads <= 0 || head_dim <= 0 || !dtype_ok(dtype)) return 0;
+    const size_t g = ikbo_glm_mlp_workspace_size(num_cand, num_req, num_glm_layers, glm_layers, dtype);
+    if (g == 0) return 0;
+    const size_t kv = align256(esize(dtype) * (size_t)(seq_rows > 0 ? seq_rows : 1) * (size_t)num_heads * (size_t)head_dim);
+    const size_t da = ikbo_dca_workspace_size(num_cand, num_req), ra = ikbo_request_attention_workspace_size(num_req);
+    return align256(g) + 2 * kv + align256(da > ra ? da : ra);
+}
+
+int ikbo_dca_layer_forward(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
+                           const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                           int32_t num_glm_layers, const ikbo_glm_layer *glm_layers, const void *seq, int64_t seq_rows,
+                           int32_t seq_dim, const int32_t *kv_cu_seqlens, int32_t kv_len, const void *w_k_cand,
+                           const void *w_v_cand, const void *w_k_req, const void *w_v_req, int32_t q_len,
+                           int32_t num_heads, int32_t head_dim, float softmax_scale, int32_t dtype, void *y_req,
+                           void *y_cand, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    const int64_t C = num_cand, R = num_req;
+    if (C < 0 || R < 0 || seq_rows < 0 || seq_dim <= 0 || q_len <= 0 || num_heads <= 0 || head_dim <= 0)
+        return fail(IKBO_INVALID_ARGUMENT, "bad sizes (num_cand %lld num_req %lld seq_rows %lld seq_dim %d q_len %d heads %d "
+                    "head_dim %d)", (long long)C, (long long)R, (long long)seq_rows, seq_dim, q_len, num_heads, head_dim);
+    if (!dtype_ok(dtype)) return fail(IKBO_UNSUPPORTED, "dtype %d", dtype);
+    if (num_glm_layers <= 0 || !glm_layers) return fail(IKBO_INVALID_ARGUMENT, "need num_glm_layers >= 1 and a host layer array");
+    const int64_t W = (int64_t)q_len * num_heads * head_dim;
+    const ikbo_glm_layer &last = glm_layers[num_glm_layers - 1];
+    if (last.n_req_out != W || last.n_cand_out != W)
+        return fail(IKBO_INVALID_ARGUMENT, "the query generator's last layer must output q_len * num_heads * head_dim = %lld "
+                    "columns per group (got %d, %d)", (long long)W, last.n_req_out, last.n_cand_out);
+    if (!kv_cu_seqlens && seq_rows != R * (int64_t)kv_len)
+        return fail(IKBO_INVALID_ARGUMENT, "seq_rows %lld must be num_req * kv_len = %lld", (long long)seq_rows,
+                    (long long)(R * (int64_t)kv_len));
+    if (R > 0 && (!y_req || !seq || !w_k_cand || !w_v_cand || !w_k_req || !w_v_req))
+        return fail(IKBO_INVALID_ARGUMENT, "y_req, seq and the four K/V weights must be non-NULL when num_req > 0");
+    if (C > 0 && !y_cand) return fail(IKBO_INVALID_ARGUMENT, "y_cand is NULL");
+    const size_t need = ikbo_dca_layer_workspace_size(C, R, num_glm_layers, glm_layers, seq_rows, num_heads, head_dim, dtype);
+    if (!workspace || workspace_bytes < need)
+        return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (!aligned16(workspace) || !aligned16(y_req) || !aligned16(y_cand))
+        return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    if ((W * (int64_t)esize(dtype)) % 16)
+        return fail(IKBO_MISALIGNED, "q_len * num_heads * head_dim must keep 16-byte halves of the output rows");
+    const size_t e = esize(dtype);
+    Carver cv(workspace);
+    const size_t g_bytes = ikbo_glm_mlp_workspace_size(C, R, num_glm_layers, glm_layers, dtype);
+    void *ws_glm = cv.take(g_bytes);
+    const size_t kv_bytes = e * (size_t)(seq_rows > 0 ? seq_rows : 1) * (size_t)num_heads * (size_t)head_dim;
+    void *kbuf = cv.take(kv_bytes), *vbuf = cv.take(kv_bytes);
+    void *ws_att = (char *)workspace + cv.used;
+    const size_t att_bytes = workspace_bytes - cv.used;
+    const int64_t ld = 2 * W;                                  // rows of [Q | A]
+    char *a_req = (char *)y_req + W * e, *a_cand = (char *)y_cand + W * e;
+    // Eq. 12: the query generator (LCB_i and MLP_i), its outputs in the left halves
+    int rc = glm_mlp_impl(x_req, R, x_cand, C, cand_to_req, req_cand_offsets, index_flags, num_glm_layers, glm_layers,
+                          dtype, dtype, y_req, y_cand, ld, ld, ws_glm, g_bytes, hip_stream);
+    if (rc) return rc;
+    if (R == 0) {
+        // no request: every candidate's attention half is zero (no valid request)
+        if (C > 0) IKBO_HIP(ikbo::launch_zero_uncovered(req_cand_offsets, 0, C, a_cand, W, ld, (int)e, (hipStream_t)hip_stream));
+        return ok();
+    }
+    // Eq. 13, candidate half: K^C, V^C of S once per request, then IKBO-DCA into the right halves
+    rc = ikbo_kv_project(seq, seq_rows, seq_dim, w_k_cand, w_v_cand, num_heads * head_dim, dtype, dtype, kbuf, vbuf,
+                         hip_stream);
+    if (rc) return rc;
+    if (C > 0) {
+        rc = dca_validate(y_cand, C, q_len, kbuf, vbuf, R, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets,
+                          index_flags, num_heads, head_dim, dtype, dtype, a_cand, ws_att, att_bytes);
+        if (rc) return rc;
+        rc = dca_run(y_cand, C, q_len, kbuf, vbuf, R, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets, num_heads,
+                     head_dim, softmax_scale, dtype, dtype, a_cand, ws_att, (hipStream_t)hip_stream, ld, ld);
+        if (rc) return rc;
+    }
+    // Eq. 13, request half: K^R, V^R (the same buffers, stream-ordered after the DCA), then A^R
+    rc = ikbo_kv_project(seq, seq_rows, seq_dim, w_k_req, w_v_req, num_heads * head_dim, dtype, dtype, kbuf, vbuf,
+                         hip_stream);
+    if (rc) return rc;
+    return request_attention_impl(y_req, R, q_len, kbuf, vbuf, kv_cu_seqlens, kv_len, num_heads, head_dim,
+                                  softmax_scale, dtype, dtype, a_req, ws_att, att_bytes, hip_stream, ld, ld);
 }
 
 int ikbo_check_index(const int32_t *cand_to_req, const int32_t *req_cand_offsets, int64_t num_cand, int64_t num_req,

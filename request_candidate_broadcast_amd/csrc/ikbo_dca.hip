@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
     if (rvalid) row_source(a, ti, srow, cand, tok);
     bf16x8 qf[KS];
     {
-        const uint16_t *qp = (const uint16_t *)a.q + ((cand * a.Lq + tok) * HD + ti.h * D) + half * 8;
+        const uint16_t *qp = (const uint16_t *)a.q + (cand * a.q_cs + tok * HD + ti.h * D) + half * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 u = rvalid ? *(const uint4 *)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
     const float l_tot = half_swap_sum(l);
     if (!rvalid) return;
     const float inv = !fits ? __builtin_nanf("") : l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int64_t obase = (cand * a.Lq + tok) * HD + ti.h * D;
+    const int64_t obase = cand * a.o_cs + tok * HD + ti.h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) void dca_f32_kernel(DcaArgs a) {
     int64_t cand = 0;
     int tok = 0;
     if (rvalid) row_source(a, ti, srow, cand, tok);
-    const float *qp = (const float *)a.q + (cand * a.Lq + tok) * HD + ti.h * D;
+    const float *qp = (const float *)a.q + cand * a.q_cs + tok * HD + ti.h * D;
     float qv[8], ov[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(256) void dca_f32_kernel(DcaArgs a) {
     }
     if (!rvalid) return;
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    const int64_t obase = (cand * a.Lq + tok) * HD + ti.h * D;
+    const int64_t obase = cand * a.o_cs + tok * HD + ti.h * D;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int e = sub + 16 * k;

@@ -650,16 +650,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int32_t tiles
 // this launch by other workgroups and are read with agent-coherent loads.
 template <bool COH = false>
 __device__ __forceinline__ void reduce_elem(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
-                                            const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1,
-                                            int64_t row, int32_t col) {
+                                            const float *bias0, int32_t act, void *out0, int32_t out0_f32, int64_t ld0,
+                                            float *out1, int64_t row, int32_t col) {
     const int64_t total = M * N, i = row * N + col;
     float s = 0.0f;
     for (int sp = 0; sp < splits; ++sp) s += COH ? load_coherent(partial + (int64_t)sp * total + i) : partial[(int64_t)sp * total + i];
     if (col < n_split) {
         float v = s + (bias0 ? bias0[col] : 0.0f);
         v = apply_act(act, v);
-        if (out0_f32) ((float *)out0)[row * n_split + col] = v;
-        else ((uint16_t *)out0)[row * n_split + col] = f32_to_bf16(v);
+        if (out0_f32) ((float *)out0)[row * ld0 + col] = v;
+        else ((uint16_t *)out0)[row * ld0 + col] = f32_to_bf16(v);
     } else {
         out1[row * (N - n_split) + (col - n_split)] = s;
     }
@@ -672,8 +672,8 @@ __device__ __forceinline__ void reduce_elem(const float *partial, int32_t splits
 constexpr int kMaxSplits = 16;
 template <bool COH = false>
 __device__ __forceinline__ void reduce_quad(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
-                                            const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1,
-                                            int64_t row, int32_t col) {
+                                            const float *bias0, int32_t act, void *out0, int32_t out0_f32, int64_t ld0,
+                                            float *out1, int64_t row, int32_t col) {
     const int64_t total = M * N, i = row * N + col;
     float4 p[kMaxSplits];
 #pragma unroll
@@ -701,8 +701,8 @@ __device__ __forceinline__ void reduce_quad(const float *partial, int32_t splits
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = apply_act(act, v[e]);
-        if (out0_f32) *(float4 *)((float *)out0 + row * n_split + col) = make_float4(v[0], v[1], v[2], v[3]);
-        else *(uint2 *)((uint16_t *)out0 + row * n_split + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        if (out0_f32) *(float4 *)((float *)out0 + row * ld0 + col) = make_float4(v[0], v[1], v[2], v[3]);
+        else *(uint2 *)((uint16_t *)out0 + row * ld0 + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     } else {
         *(float4 *)(out1 + row * (N - n_split) + (col - n_split)) = make_float4(v[0], v[1], v[2], v[3]);
     }
@@ -713,19 +713,20 @@ __device__ __forceinline__ bool reduce_quads_ok(int32_t splits, int32_t N, int32
 }
 
 __global__ void splitk_reduce_kernel(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
-                                     const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1) {
+                                     const float *bias0, int32_t act, void *out0, int32_t out0_f32, int64_t ld0,
+                                     float *out1) {
     const int64_t total = M * N;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     if (reduce_quads_ok(splits, N, n_split)) {
         for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < total / 4; q += stride) {
             const int64_t row = 4 * q / N;
-            reduce_quad(partial, splits, M, N, n_split, bias0, act, out0, out0_f32, out1, row, (int32_t)(4 * q - row * N));
+            reduce_quad(partial, splits, M, N, n_split, bias0, act, out0, out0_f32, ld0, out1, row, (int32_t)(4 * q - row * N));
         }
         return;
     }
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += stride) {
         const int64_t row = i / N;
-        reduce_elem(partial, splits, M, N, n_split, bias0, act, out0, out0_f32, out1, row, (int32_t)(i - row * N));
+        reduce_elem(partial, splits, M, N, n_split, bias0, act, out0, out0_f32, ld0, out1, row, (int32_t)(i - row * N));
     }
 }
 
@@ -837,7 +838,7 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
                         const int col = n0 + 4 * (i % (BN / 4));
                         if (row < rq.M && col < rq.N)
                             reduce_quad<true>(rq.partial, splits, rq.M, rq.N, f.n_split, f.bias0, f.act, f.out0,
-                                              f.out0_f32, z, row, col);
+                                              f.out0_f32, f.n_split, z, row, col);
                     }
                 } else {
                     for (int i = tid; i < BM * BN; i += kGemmThreads) {
@@ -845,7 +846,7 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
                         const int col = n0 + i % BN;
                         if (row < rq.M && col < rq.N)
                             reduce_elem<true>(rq.partial, splits, rq.M, rq.N, f.n_split, f.bias0, f.act, f.out0,
-                                              f.out0_f32, z, row, col);
+                                              f.out0_f32, f.n_split, z, row, col);
                     }
                 }
                 wait_vmcnt<0>();                   // Z and Y_r have reached the L2 ...
@@ -1030,14 +1031,14 @@ hipError_t launch_lcb_fused(const LcbFusedArgs &f, hipStream_t s) {
 }
 
 hipError_t launch_splitk_reduce(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
-                                const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1,
-                                hipStream_t s) {
+                                const float *bias0, int32_t act, void *out0, int32_t out0_f32, int64_t ld0,
+                                float *out1, hipStream_t s) {
     const int64_t total = M * N;
     if (total <= 0) return hipSuccess;
     int64_t g = (total + 255) / 256;
     if (g > 65536) g = 65536;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)g), dim3(256), 0, s, partial, splits, M, N, n_split, bias0,
-                       act, out0, out0_f32, out1);
+                       act, out0, out0_f32, ld0, out1);
     return hipGetLastError();
 }
 

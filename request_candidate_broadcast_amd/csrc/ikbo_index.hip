@@ -89,14 +89,14 @@ __global__ __launch_bounds__(1024) void scan_tiles_kernel(const int32_t *counts,
 }
 
 __global__ void scatter_kernel(const int32_t *m, int64_t C, int64_t R, int32_t *cursor, int32_t *perm, void *out,
-                               int64_t row_elems, int out_bytes) {
+                               int64_t row_elems, int64_t row_stride, int out_bytes) {
     for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < C; c += (int64_t)gridDim.x * blockDim.x) {
         const int32_t r = m[c];
         if (r >= 0 && r < R) {
             const int32_t pos = atomicAdd(&cursor[r], 1);
             perm[pos] = (int32_t)c;
         } else if (out) {
-            char *row = (char *)out + c * row_elems * out_bytes;
+            char *row = (char *)out + c * row_stride * out_bytes;
             for (int64_t i = 0; i < row_elems * out_bytes; i += 4) *(uint32_t *)(row + i) = 0u;
         }
     }
@@ -119,13 +119,13 @@ __global__ void offsets_to_map_kernel(const int32_t *off, int64_t R, int64_t C, 
 }
 
 __global__ void zero_uncovered_kernel(const int32_t *off, int64_t R, int64_t C, void *out, int64_t row_elems,
-                                      int out_bytes) {
+                                      int64_t row_stride, int out_bytes) {
     const int64_t c0 = R > 0 ? clampi(off[0], 0, C) : C;
     const int64_t c1 = R > 0 ? clampi(off[R], c0, C) : C;
     const int64_t words = row_elems * out_bytes / 4;
     for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < C; c += (int64_t)gridDim.x * blockDim.x) {
         if (c >= c0 && c < c1) continue;
-        uint32_t *row = (uint32_t *)out + c * words;
+        uint32_t *row = (uint32_t *)((char *)out + c * row_stride * out_bytes);
         for (int64_t i = 0; i < words; ++i) row[i] = 0u;
     }
 }
@@ -190,10 +190,10 @@ hipError_t launch_scan_tiles(const int32_t *counts, const int32_t *off_in, int64
 }
 
 hipError_t launch_scatter(const int32_t *m, int64_t C, int64_t R, int32_t *cursor, int32_t *perm, void *out,
-                          int64_t row_elems, int out_bytes, hipStream_t s) {
+                          int64_t row_elems, int64_t row_stride, int out_bytes, hipStream_t s) {
     if (C <= 0) return hipSuccess;
     hipLaunchKernelGGL(scatter_kernel, dim3(grid_for(C, 256)), dim3(256), 0, s, m, C, R, cursor, perm, out,
-                       row_elems, out_bytes);
+                       row_elems, row_stride, out_bytes);
     return hipGetLastError();
 }
 
@@ -204,10 +204,10 @@ hipError_t launch_offsets_to_map(const int32_t *off, int64_t R, int64_t C, int32
 }
 
 hipError_t launch_zero_uncovered(const int32_t *off, int64_t R, int64_t C, void *out, int64_t row_elems,
-                                 int out_bytes, hipStream_t s) {
+                                 int64_t row_stride, int out_bytes, hipStream_t s) {
     if (C <= 0) return hipSuccess;
     hipLaunchKernelGGL(zero_uncovered_kernel, dim3(grid_for(C, 256)), dim3(256), 0, s,
-                       off, R, C, out, row_elems, out_bytes);
+                       off, R, C, out, row_elems, row_stride, out_bytes);
     return hipGetLastError();
 }
 

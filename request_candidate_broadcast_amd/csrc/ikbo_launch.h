@@ -21,14 +21,15 @@ hipError_t launch_scan_tiles(const int32_t *counts, const int32_t *off_in, int64
                              int32_t heads, int32_t block_m, int32_t *off_out, int32_t *cursor,
                              int32_t *tile_start, hipStream_t s);
 // perm[cursor[m[c]]++] = c for valid m; rows of candidates with invalid m are zeroed in `out`
-// (row width row_elems, element size out_bytes).
+// (row_elems elements of out_bytes each, rows row_stride elements apart).
 hipError_t launch_scatter(const int32_t *m, int64_t C, int64_t R, int32_t *cursor, int32_t *perm, void *out,
-                          int64_t row_elems, int out_bytes, hipStream_t s);
+                          int64_t row_elems, int64_t row_stride, int out_bytes, hipStream_t s);
 // m_out[c] = r with off[r] <= c < off[r+1] (binary search over a sanitised view), -1 when none.
 hipError_t launch_offsets_to_map(const int32_t *off, int64_t R, int64_t C, int32_t *m_out, hipStream_t s);
-// Zero rows of `out` for candidates outside [clamp(off[0]), clamp(off[R])).
+// Zero rows of `out` for candidates outside [clamp(off[0]), clamp(off[R])) (row_elems elements,
+// rows row_stride elements apart).
 hipError_t launch_zero_uncovered(const int32_t *off, int64_t R, int64_t C, void *out, int64_t row_elems,
-                                 int out_bytes, hipStream_t s);
+                                 int64_t row_stride, int out_bytes, hipStream_t s);
 hipError_t launch_check_index(const int32_t *m, const int32_t *off, int64_t C, int64_t R, uint32_t flags,
                               uint64_t *d_count, hipStream_t s);
 
@@ -46,6 +47,7 @@ struct DcaArgs {
     float scale;
     int32_t in_f32, out_f32;
     int32_t small;              // bf16: the one-wave configuration (32 rows per work tile)
+    int64_t q_cs, o_cs;         // elements from one candidate's q (out) rows to the next's (>= Lq H D)
 };
 // Rows of stacked candidate queries covered by one DCA work tile, per path.
 int32_t dca_block_m(int32_t D, int in_f32, int small);
@@ -76,10 +78,11 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
 // Sum the split-K partials in a fixed order, then columns n < n_split go to out0 = act(sum + bias0)
-// ([M, n_split], out dtype) and columns n >= n_split go to out1 = sum (fp32, [M, N - n_split]).
+// ([M, n_split] with row stride ld0, out dtype) and columns n >= n_split go to out1 = sum (fp32,
+// [M, N - n_split]).
 hipError_t launch_splitk_reduce(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
-                                const float *bias0, int32_t act, void *out0, int32_t out0_f32, float *out1,
-                                hipStream_t s);
+                                const float *bias0, int32_t act, void *out0, int32_t out0_f32, int64_t ld0,
+                                float *out1, hipStream_t s);
 // Split count the request GEMM uses for an M x N x K problem.
 int32_t request_gemm_splits(int64_t M, int32_t N, int32_t K, int in_f32);
 
