@@ -31,6 +31,31 @@ FM_SHAPE = (128, 2048, 32, 32, 64)   # requests, candidates per request, n_r, n_
 LCBE_SHAPE = (128, 2048, 32, 32, 64, 32, 32)
 
 
+def stack_layer2(np, synth, s):
+    """The second interaction layer of the stack workload: its query generator reads the first
+    layer's [Q | A] rows (2 W = 8192 wide per group): [8192 | 8192] -> 2048 (GELU) -> 4096, weights
+    N(0, 1/fan-in), biases N(0, 1/fan-in); its own sequence rows S_2 (N(0, 1)) and K/V weights
+    N(0, 1/1024)."""
+    W = s.Lq * s.H * s.d
+    hd, rows = s.H * s.d, s.kv_rows
+    layers = []
+    for i, (kr, kc, n, act) in enumerate(((2 * W, 2 * W, 2048, "gelu"), (2048, 2048, W, "none"))):
+        t = 200 + 8 * i
+        layers.append(dict(w_rr=synth.draw(7, t, n * kr, "bf16", 1 / np.sqrt(kr)).reshape(n, kr),
+                           w_cr=synth.draw(7, t + 1, n * kr, "bf16", 1 / np.sqrt(kr)).reshape(n, kr),
+                           w_cc=synth.draw(7, t + 2, n * kc, "bf16", 1 / np.sqrt(kc)).reshape(n, kc),
+                           b_r=synth.draw(7, t + 3, n, "f32", 1 / np.sqrt(kr)),
+                           b_c=synth.draw(7, t + 4, n, "f32", 1 / np.sqrt(kc)), act=act))
+    seq = lambda start=0, count=rows: synth.draw(7, 220, count * hd, "bf16", 1.0, start=start * hd).reshape(count, hd)
+    kv = [synth.draw(7, 221 + i, hd * hd, "bf16", 1 / np.sqrt(hd)).reshape(hd, hd) for i in range(4)]
+    return layers, seq, kv
+
+
+def mlp_flops(C, R, layers):
+    """2 C sum k_c n_c + 2 R sum k_r (n_r + n_c) over GLM layers given as (k_r, k_c, n_r, n_c)."""
+    return sum(2.0 * C * kc * nc + 2.0 * R * kr * (nr + nc) for kr, kc, nr, nc in layers)
+
+
 def lcbe_params(np, synth):
     """Weights N(0, 1/n_in) and per-group gamma, beta of the LCB embedding-form workload."""
     import math
@@ -49,7 +74,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="block", choices=["block", "layer", "dca_fixed", "dca_ragged", "lcb", "fm", "lcb_emb"])
+    p.add_argument("--workload", default="block", choices=["block", "layer", "dca_fixed", "dca_ragged", "lcb", "fm", "lcb_emb",
+                                                           "stack"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=0, help="candidates in the oracle sample (0 = default)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -213,6 +239,53 @@ def main():
             dominant = "fm"
             config = {"workload": "GLM factorization machine (two groups, in-kernel broadcast)", "requests": R,
                       "candidates": C, "n_req_feat": n_r, "n_cand_feat": n_c, "dim": d}
+        elif args.workload == "stack":
+            # two DCA interaction layers (Eq. 12-13 and the [Q | A] rows that feed the next), one
+            # ikbo_dca_layer_forward call each: the block's layer, then a layer reading its output
+            g, s = synth.block_specs()
+            W, hd, rows = s.Lq * s.H * s.d, s.H * s.d, s.kv_rows
+            x_r = up(synth.glm_x(g, "x_r"))
+            x_c = up(synth.glm_x(g, "x_c"))
+            l1 = []
+            for li in range(len(g.layers)):
+                w = synth.glm_weights(g, li)
+                l1.append({"w_rr": up(w["w_rr"]), "w_cr": up(w["w_cr"]), "w_cc": up(w["w_cc"]),
+                           "b_r": up(w["b_r"]), "b_c": up(w["b_c"]), "act": g.layers[li].act})
+            s1 = up(synth.seq_rows(s))
+            kv1 = [up(synth.kv_weight(s, n)) for n in ("w_kc", "w_vc", "w_kr", "w_vr")]
+            l2h, seq2, kv2h = stack_layer2(np, synth, s)
+            l2 = [{kk: (up(vv) if isinstance(vv, np.ndarray) else vv) for kk, vv in ly.items()} for ly in l2h]
+            s2 = up(seq2())
+            kv2 = [up(w) for w in kv2h]
+            off = up(s.offsets)
+            y1_r = torch.empty((s.R, 2 * W), dtype=torch.bfloat16, device=dev)
+            y1_c = torch.empty((s.C, 2 * W), dtype=torch.bfloat16, device=dev)
+            y2_r, y2_c = torch.empty_like(y1_r), torch.empty_like(y1_c)
+            nbytes = max(ikbo.load_library().ikbo_dca_layer_workspace_size(s.C, s.R, len(ls), ikbo._layer_structs(ls),
+                                                                           rows, s.H, s.d, ikbo.IKBO_BF16)
+                         for ls in (l1, l2))
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            attn = 2 * 2 * 2.0 * rows * hd * hd + s.flops() + 4.0 * s.R * s.Lq * s.H * s.d * s.L
+            ly0, ly1 = g.layers
+            flops["layer1"] = mlp_flops(s.C, s.R, [(ly0.k_req, ly0.k_cand, ly0.n_req, ly0.n_cand),
+                                                    (ly1.k_req, ly1.k_cand, ly1.n_req, ly1.n_cand)]) + attn
+            flops["layer2"] = mlp_flops(s.C, s.R, [(2 * W, 2 * W, 2048, 2048), (2048, 2048, W, W)]) + attn
+            algo_bytes["layer1"] = algo_bytes["layer2"] = 0
+            kw = dict(q_len=s.Lq, num_heads=s.H, head_dim=s.d, req_cand_offsets=off, workspace=ws, stream=stream)
+
+            def step(ev):
+                ev[0].record(stream)
+                ikbo.ikbo_dca_layer_forward(x_r, x_c, l1, s1, *kv1, y_req=y1_r, y_cand=y1_c, **kw)
+                ev[1].record(stream)
+                ikbo.ikbo_dca_layer_forward(y1_r, y1_c, l2, s2, *kv2, y_req=y2_r, y_cand=y2_c, **kw)
+                ev[2].record(stream)
+
+            names = [("layer1", 0, 1), ("layer2", 1, 2)]
+            dominant = "layer2"
+            config = {"workload": "ROCS interaction stack: 2 DCA layers (GLM-MLP -> K/V of S -> A^C + A^R, "
+                      "[Q | A] to the next layer), one call per layer", "requests": s.R, "candidates": s.C,
+                      "mlp_layer1": "[4096|2048] -> 2048 (GELU) -> 4096", "mlp_layer2": "[8192|8192] -> 2048 (GELU) -> 4096",
+                      "kv_len": s.L, "heads": s.H, "head_dim": s.d, "q_tokens": s.Lq, "seq_width": hd}
         elif args.workload == "lcb_emb":
             # LCB embedding form (Eq. 5-6) with a per-group LayerNorm (Eq. 7) on the block's batch:
             # 128 requests x 2048 candidates, 32 -> 32 embeddings of width 64 per group, bf16 in and out
@@ -354,6 +427,8 @@ def main():
     roofline = roofline or {"bound": "mfma", "achieved": round(dk["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(dk["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": dominant, "flops_per_launch": flops[dominant], "ms_per_launch": round(dk["ms_avg"], 4)}
+    if args.workload == "stack":
+        roofline["kernel"] = "layer2: one ikbo_dca_layer_forward call (11 launches; its DCA alone is the block workload's)"
 
     # IKBO-LCB also has a persistent request/candidate launch (IKBO_LCB_FUSED=1, same bits); time it
     # after the timed region, on the same inputs, for comparison
@@ -445,6 +520,34 @@ def cpu_baseline(args, np):
         secs = time.perf_counter() - t0
         work = 2.0 * len(m_sub) * n_c * (n_r + n_c) * d
         sample = "%d candidates (the first %d of each of the %d requests)" % (len(m_sub), n_per, len(reqs))
+    elif args.workload == "stack":
+        g, s = synth.block_specs()
+        r0 = 0
+        n = args.cpu_sample if args.cpu_sample else 64
+        cands = np.arange(s.offsets[r0], s.offsets[r0] + n)
+        W, hd = s.Lq * s.H * s.d, s.H * s.d
+        # request 0's rows of every input, then both layers on the sample (the first layer's output
+        # goes to the second as fp32)
+        x_r = synth.glm_x(g, "x_r", r0, 1)
+        x_c = synth.glm_x(g, "x_c", int(cands[0]), n)
+        l1 = [dict(synth.glm_weights(g, li), act=g.layers[li].act) for li in range(len(g.layers))]
+        l2h, seq2, kv2h = stack_layer2(np, synth, s)
+        m1 = np.zeros(n, np.int32)
+        t0 = time.perf_counter()
+        y1 = oracle.dca_layer(x_r, x_c, l1, synth.seq_rows(s, r0 * s.L, s.L),
+                              *[synth.kv_weight(s, nm) for nm in ("w_kc", "w_vc", "w_kr", "w_vr")],
+                              q_len=s.Lq, heads=s.H, m=m1, nthreads=nthreads)
+        f32 = lambda a: oracle.decode(a).astype(np.float32)
+        l2 = [{k: (f32(v) if k in ("w_rr", "w_cr", "w_cc") else v) for k, v in ly.items()} for ly in l2h]
+        oracle.dca_layer(y1["y_r"].astype(np.float32), y1["y_c"].astype(np.float32), l2, f32(seq2(r0 * s.L, s.L)),
+                         *[f32(w) for w in kv2h], q_len=s.Lq, heads=s.H, m=m1, nthreads=nthreads)
+        secs = time.perf_counter() - t0
+        attn_req = 2 * 2 * 2.0 * s.L * hd * hd + 4.0 * s.Lq * s.H * s.d * s.L
+        attn_c = 4.0 * s.Lq * s.H * s.d * s.L
+        ly0, ly1 = g.layers
+        work = (mlp_flops(n, 1, [(ly0.k_req, ly0.k_cand, ly0.n_req, ly0.n_cand), (ly1.k_req, ly1.k_cand, ly1.n_req, ly1.n_cand)])
+                + mlp_flops(n, 1, [(2 * W, 2 * W, 2048, 2048), (2048, 2048, W, W)]) + 2 * (attn_req + n * attn_c))
+        sample = "request %d and its first %d candidates through both layers" % (r0, n)
     elif args.workload == "lcb_emb":
         R, per_r, n_r, n_c, d, k_r, k_c = LCBE_SHAPE
         # every request and all their candidates: the whole workload (a few seconds of oracle work)
