@@ -107,7 +107,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
