@@ -324,12 +324,16 @@ static int dca_run(const void *q, int64_t C, int32_t q_len, const void *k, const
     if (o_cs == 0) o_cs = row_elems;
     const int ob = (int)esize(out_dtype);
     // few stacked query rows per request (at most 32 on average): one-wave, 32-row work tiles
-    const int small = !in_f32 && C * (int64_t)q_len <= 32 * R;
+    // work tile by the average stacked query rows per request: at most 32 one wave, at most 1024
+    // four waves (128 rows), else eight (256 rows); a request's last tile is partly empty, and
+    // smaller tiles waste fewer rows where requests are short
+    const int64_t rows_all = C * (int64_t)q_len;
+    const int mode = in_f32 ? 0 : rows_all <= 32 * R ? 1 : rows_all <= 1024 * R ? 2 : 0;
 
     Carver cv(workspace);
     int32_t *counts, *off, *tiles, *perm;
     dca_ws(C, R, &cv, &counts, &off, &tiles, &perm);
-    const int32_t bm = ikbo::dca_block_m(head_dim, in_f32, small);
+    const int32_t bm = ikbo::dca_block_m(head_dim, in_f32, mode);
     const int32_t *perm_used = nullptr;
     if (req_cand_offsets) {
         IKBO_HIP(ikbo::launch_scan_tiles(nullptr, req_cand_offsets, R, C, q_len, num_heads, bm, off, nullptr, tiles, s));
@@ -362,7 +366,7 @@ static int dca_run(const void *q, int64_t C, int32_t q_len, const void *k, const
     a.scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
     a.in_f32 = in_f32;
     a.out_f32 = out_dtype == IKBO_F32;
-    a.small = small;
+    a.mode = mode;
     a.q_cs = q_cs;
     a.o_cs = o_cs;
     IKBO_HIP(ikbo::launch_dca(a, s));

@@ -463,12 +463,14 @@ __global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
 }
 
 // The configurations the library launches, per head dim: 8 waves x 32 query rows, 64-key tiles,
-// two LDS stages, K reads two k16 steps ahead; and, for requests with few stacked query rows (the
-// request-side attention has q_len rows per request), one wave of 32 rows, so a work tile is not
-// mostly empty rows (each row's arithmetic is the same in both, so are the results).
-template <int D, bool SMALL = false>
+// two LDS stages, K reads two k16 steps ahead (mode 0); for requests with a few hundred stacked
+// query rows, 4 waves of 32 rows, two workgroups per CU (mode 2: a request's last work tile is
+// on average half as empty); and for requests with very few rows (the request-side attention has
+// q_len rows per request), one wave of 32 rows (mode 1). Each row's arithmetic is the same in all
+// three, so are the results.
+template <int D, int MODE = 0>
 struct DcaBf16Config {
-    static constexpr int NW = SMALL ? 1 : 8, NKB = 2, NBUF = 2, KPD = 1, VPD = 1, COPYAT = 0;
+    static constexpr int NW = MODE == 1 ? 1 : MODE == 2 ? 4 : 8, NKB = 2, NBUF = 2, KPD = 1, VPD = 1, COPYAT = 0;
     static constexpr int BM = NW * 32;
 };
 
@@ -561,9 +563,10 @@ __global__ __launch_bounds__(256) void dca_f32_kernel(DcaArgs a) {
 
 }  // namespace
 
-int32_t dca_block_m(int32_t D, int in_f32, int small) {
+int32_t dca_block_m(int32_t D, int in_f32, int mode) {
     if (in_f32) return kF32Rows;
-    if (small) return D == 128 ? DcaBf16Config<128, true>::BM : DcaBf16Config<64, true>::BM;
+    if (mode == 1) return D == 128 ? DcaBf16Config<128, 1>::BM : DcaBf16Config<64, 1>::BM;
+    if (mode == 2) return D == 128 ? DcaBf16Config<128, 2>::BM : DcaBf16Config<64, 2>::BM;
     return D == 128 ? DcaBf16Config<128>::BM : DcaBf16Config<64>::BM;
 }
 
@@ -581,11 +584,13 @@ hipError_t launch_dca(const DcaArgs &a, hipStream_t s) {
                            dim3(C::NW * 64), 0, s, a);                                                                 \
     } while (0)
         if (a.D == 128) {
-            if (a.small) IKBO_DCA_LAUNCH(128, true);
-            else IKBO_DCA_LAUNCH(128, false);
+            if (a.mode == 1) IKBO_DCA_LAUNCH(128, 1);
+            else if (a.mode == 2) IKBO_DCA_LAUNCH(128, 2);
+            else IKBO_DCA_LAUNCH(128, 0);
         } else {
-            if (a.small) IKBO_DCA_LAUNCH(64, true);
-            else IKBO_DCA_LAUNCH(64, false);
+            if (a.mode == 1) IKBO_DCA_LAUNCH(64, 1);
+            else if (a.mode == 2) IKBO_DCA_LAUNCH(64, 2);
+            else IKBO_DCA_LAUNCH(64, 0);
         }
 #undef IKBO_DCA_LAUNCH
     } else {

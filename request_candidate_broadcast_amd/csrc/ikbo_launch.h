@@ -46,11 +46,11 @@ struct DcaArgs {
     int64_t grid_tiles;         // upper bound on tile_start[R], sizes the grid
     float scale;
     int32_t in_f32, out_f32;
-    int32_t small;              // bf16: the one-wave configuration (32 rows per work tile)
+    int32_t mode;               // bf16 work tile: 0 eight waves (256 rows), 1 one wave (32), 2 four waves (128)
     int64_t q_cs, o_cs;         // elements from one candidate's q (out) rows to the next's (>= Lq H D)
 };
 // Rows of stacked candidate queries covered by one DCA work tile, per path.
-int32_t dca_block_m(int32_t D, int in_f32, int small);
+int32_t dca_block_m(int32_t D, int in_f32, int mode);
 hipError_t launch_dca(const DcaArgs &a, hipStream_t s);
 
 // ---- GEMMs for IKBO-LCB (ikbo_gemm.hip) ------------------------------------------------------
