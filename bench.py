@@ -77,6 +77,7 @@ def parse():
     p.add_argument("--workload", default="block", choices=["block", "layer", "dca_fixed", "dca_ragged", "lcb", "fm", "lcb_emb",
                                                            "stack"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA / HBM / exp2 ceilings")
     p.add_argument("--cpu-sample", type=int, default=0, help="candidates in the oracle sample (0 = default)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="per-kernel HBM bytes measured with rocprofv3 counters, if present")
@@ -447,6 +448,18 @@ def main():
         finally:
             os.environ.pop("IKBO_LCB_FUSED", None)
 
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(torch, ikbo, stream)
+        log("ceilings: %s" % ceilings)
+        if "dca" in per:
+            # one exp2 per score (the fixed-reference softmax), FLOPs = 4 d per score
+            d_head = config.get("head_dim", 128)
+            exps = flops["dca"] / (4.0 * d_head)
+            per["dca"]["exps_per_s"] = exps / (per["dca"]["ms_avg"] * 1e-3)
+            per["dca"]["exp_frac_of_measured"] = per["dca"]["exps_per_s"] / ceilings["exp2_per_s"]
+        roofline["measured_peak"] = (ceilings["mfma_bf16_tflops"] if roofline["bound"] == "mfma"
+                                     else ceilings["hbm_copy_gbs"])
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, np)
@@ -457,11 +470,50 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded SplitMix64 normals)",
         "config": config,
         "parts": {k: {kk: round(vv, 4) for kk, vv in d.items()} for k, d in per.items()},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "ceilings": ceilings,
     }
     if alt:
         line["alternate_forms"] = alt
     print(json.dumps(line), flush=True)
+
+
+def measure_ceilings(torch, ikbo, stream):
+    """What kernels of this part reach on their own (libikbo_probe.so), beside the published peaks:
+    dense bf16 MFMA from register operands, HBM copy and read streams, v_exp_f32 evaluations.
+    Median of 5 timed launches after one warm-up each."""
+    dev = torch.device("cuda:0")
+
+    def timed(kind, buf, iters, blocks):
+        ikbo.ikbo_probe_launch(kind, buf, iters, blocks, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for i in range(5):
+            ev[i].record(stream)
+            ikbo.ikbo_probe_launch(kind, buf, iters, blocks, stream)
+        ev[5].record(stream)
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(5))[2] * 1e-3
+
+    out = {}
+    small = torch.empty(4096 * 1024, dtype=torch.uint8, device=dev)
+    best = 0.0
+    for blocks in (512, 1024):                 # 2 and 4 waves per SIMD
+        iters = 20000
+        sec = timed(ikbo.IKBO_PROBE_MFMA_BF16, small, iters, blocks)
+        best = max(best, blocks * 4 * iters * 4 * 32768.0 / sec / 1e12)
+    out["mfma_bf16_tflops"] = round(best, 1)
+    iters, blocks = 8000, 2048
+    sec = timed(ikbo.IKBO_PROBE_EXP2, small, iters, blocks)
+    out["exp2_per_s"] = float("%.4g" % (blocks * 256 * iters * 8 / sec))
+    big = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    big.zero_()
+    # 1 GiB read + 1 GiB written; the best of three grid sizes (one to four rounds of resident waves)
+    out["hbm_copy_gbs"] = round(max(2 * (1 << 30) / timed(ikbo.IKBO_PROBE_COPY, big, 0, b) / 1e9
+                                    for b in (2048, 4096, 8192)), 1)
+    out["hbm_read_gbs"] = round(max(((2 << 30) - b * 1024) / timed(ikbo.IKBO_PROBE_READ, big, 0, b) / 1e9
+                                    for b in (2048, 4096, 8192)), 1)
+    del big
+    out["spec"] = {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
+    return out
 
 
 def cpu_baseline(args, np):

@@ -1,0 +1,38 @@
+/*
+ * ikbo_probe.h -- ceiling probes for the roofline (libikbo_probe.so, gfx950). Not part of the
+ * method: they measure what a kernel of this part reaches for bf16 dense MFMA, HBM streaming and
+ * the transcendental unit, to report beside the published peaks.
+ *
+ * ikbo_probe_launch enqueues one probe on hip_stream (a hipStream_t; NULL = default stream) and
+ * returns 0, or 1 for a bad argument and 5 for a failed launch. Work per launch:
+ *   IKBO_PROBE_MFMA_BF16  blocks * 4 waves * iters * 4 * 32768 FLOP; writes blocks * 256 floats
+ *                         to buf (bytes >= blocks * 1024)
+ *   IKBO_PROBE_EXP2       blocks * 256 threads * iters * 8 exp2 evaluations; same output
+ *   IKBO_PROBE_COPY       copies the first bytes / 2 of buf (rounded down to 16) onto the
+ *                         second half: that many bytes read and written
+ *   IKBO_PROBE_READ       reads buf except its last blocks * 1024 bytes, which receive one word
+ *                         per thread
+ * buf: device memory, 16-byte aligned, owned by the caller. iters >= 0; 1 <= blocks < 2^31.
+ */
+#ifndef IKBO_PROBE_H
+#define IKBO_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IKBO_PROBE_MFMA_BF16 0
+#define IKBO_PROBE_EXP2 1
+#define IKBO_PROBE_COPY 2
+#define IKBO_PROBE_READ 3
+
+int ikbo_probe_launch(int32_t kind, void *buf, size_t bytes, int64_t iters, int64_t blocks, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

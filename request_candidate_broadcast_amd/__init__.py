@@ -63,6 +63,32 @@ EXPORTS = ["ikbo_version", "ikbo_status_string", "ikbo_last_error_message",
 _lib = None
 
 
+PROBE_PATH = os.path.join(PKG_DIR, "libikbo_probe.so")
+IKBO_PROBE_MFMA_BF16, IKBO_PROBE_EXP2, IKBO_PROBE_COPY, IKBO_PROBE_READ = 0, 1, 2, 3
+_probe = None
+
+
+def load_probe(path: str = PROBE_PATH) -> ctypes.CDLL:
+    """The roofline ceiling probes (libikbo_probe.so, include/ikbo_probe.h); not part of the method."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(path):
+            raise RuntimeError("libikbo_probe.so is not built at %s" % path)
+        lib = ctypes.CDLL(path)
+        lib.ikbo_probe_launch.restype = ctypes.c_int
+        lib.ikbo_probe_launch.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_void_p]
+        _probe = lib
+    return _probe
+
+
+def ikbo_probe_launch(kind: int, buf: torch.Tensor, iters: int, blocks: int, stream=None) -> None:
+    st = load_probe().ikbo_probe_launch(kind, _ptr(buf), buf.numel() * buf.element_size(), iters, blocks,
+                                        _stream(stream))
+    if st != 0:
+        raise IkboError("ikbo_probe_launch(kind %d) failed with status %d" % (kind, st))
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libikbo.so and declare its C signatures. Raises when it has not been built."""
     global _lib

@@ -11,6 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libikbo.so")
+PROBE_DIR = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libikbo_probe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("IKBO_OFFLOAD_ARCH", "gfx950")
 
@@ -39,21 +41,36 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every csrc/*.hip and link libikbo.so. Always rebuilds."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
     # --no-undefined: a kernel whose host launch stub was not emitted fails here, not at dlopen
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build_probe(verbose: bool = True) -> str:
+    """Compile probe/*.hip (the roofline ceiling probes) into libikbo_probe.so."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sorted(os.path.join(PROBE_DIR, f) for f in os.listdir(PROBE_DIR) if f.endswith(".hip"))
+    _link([_compile(s) for s in srcs], PROBE_LIB)
+    if verbose:
+        print("built", PROBE_LIB)
+    return PROBE_LIB
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every csrc/*.hip and link libikbo.so, then the probe library. Always rebuilds."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs, LIB)
     if verbose:
         print("built", LIB)
+    build_probe(verbose)
     return LIB
 
 

@@ -1,0 +1,137 @@
+// Ceiling probes for the roofline: the rates a kernel of this part can reach on its own, measured
+// beside the published peaks (bf16 dense MFMA, HBM, and the transcendental unit the softmax uses).
+// Each probe is a bounded loop over registers or a grid-stride pass over a buffer; none depends
+// on the method. The caller times the launch (events on the stream) and divides the work below.
+#include "ikbo_probe.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Four independent v_mfma_f32_32x32x16_bf16 chains per wave, `iters` rounds: 4 * 32768 FLOP per
+// wave per round. Operands come from the lane index so nothing folds; one float per thread is
+// stored so nothing is dropped.
+__global__ __launch_bounds__(256) void probe_mfma_kernel(float *out, int64_t iters) {
+    const int lane = threadIdx.x & 63;
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(1e-3f * (float)((lane + e) & 7));
+        b[e] = (__bf16)(1e-3f * (float)((lane * 3 + e) & 7));
+    }
+    f32x16 c0, c1, c2, c3;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c0[e] = c1[e] = c2[e] = c3[e] = 0.0f;
+    for (int64_t i = 0; i < iters; ++i) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += c0[e] + c1[e] + c2[e] + c3[e];
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// Eight independent chains y <- 2^(-y) per thread (y stays in [0.5, 1]): 8 v_exp_f32 per thread
+// per round, the negation folded into the instruction.
+__global__ __launch_bounds__(256) void probe_exp2_kernel(float *out, int64_t iters) {
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = 0.5f + 0.01f * (float)((threadIdx.x + k) & 31);
+    for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = __builtin_amdgcn_exp2f(-y[k]);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += y[k];
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// Chunk k (< 4) of lane l of wave w in step j: each wave owns 256 consecutive 16-byte chunks per
+// step (4 KiB), each of its 4 loads a contiguous 1 KiB, and the waves of the grid cover 4 * nthr
+// consecutive chunks per step.
+__device__ __forceinline__ int64_t probe_chunk(int64_t j, int64_t nthr, int64_t t, int k) {
+    return j * 4 * nthr + (t >> 6) * 256 + k * 64 + (t & 63);
+}
+
+// dst <- src with four 16-byte loads in flight per lane (all issued before the stores); chunks past
+// the last whole step are copied one per lane.
+__global__ __launch_bounds__(256) void probe_copy_kernel(const uint4 *src, uint4 *dst, int64_t n16) {
+    const int64_t nthr = (int64_t)gridDim.x * blockDim.x, t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t steps = n16 / (4 * nthr);
+    for (int64_t j = 0; j < steps; ++j) {
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = src[probe_chunk(j, nthr, t, k)];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[probe_chunk(j, nthr, t, k)] = v[k];
+    }
+    for (int64_t i = steps * 4 * nthr + t; i < n16; i += nthr) dst[i] = src[i];
+}
+
+// Reads src once, four 16-byte loads in flight per lane, one word per thread written.
+__global__ __launch_bounds__(256) void probe_read_kernel(const uint4 *src, int64_t n16, uint32_t *out) {
+    const int64_t nthr = (int64_t)gridDim.x * blockDim.x, t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t steps = n16 / (4 * nthr);
+    uint32_t x = 0;
+    for (int64_t j = 0; j < steps; ++j) {
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = src[probe_chunk(j, nthr, t, k)];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+    for (int64_t i = steps * 4 * nthr + t; i < n16; i += nthr) {
+        const uint4 v = src[i];
+        x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    out[t] = x;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ikbo_probe_launch(int32_t kind, void *buf, size_t bytes, int64_t iters, int64_t blocks, void *hip_stream) {
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (!buf || blocks <= 0 || blocks > 0x7fffffffLL || iters < 0) return 1;
+    const dim3 grid((unsigned)blocks), block(256);
+    const size_t per_thread_out = (size_t)blocks * 256 * 4;
+    switch (kind) {
+        case IKBO_PROBE_MFMA_BF16:
+            if (bytes < per_thread_out) return 1;
+            hipLaunchKernelGGL(probe_mfma_kernel, grid, block, 0, s, (float *)buf, iters);
+            break;
+        case IKBO_PROBE_EXP2:
+            if (bytes < per_thread_out) return 1;
+            hipLaunchKernelGGL(probe_exp2_kernel, grid, block, 0, s, (float *)buf, iters);
+            break;
+        case IKBO_PROBE_COPY: {
+            // the first half of buf is copied onto the second half
+            const int64_t n16 = (int64_t)(bytes / 2 / 16);
+            if (n16 <= 0 || ((uintptr_t)buf & 15)) return 1;
+            hipLaunchKernelGGL(probe_copy_kernel, grid, block, 0, s, (const uint4 *)buf, (uint4 *)buf + n16, n16);
+            break;
+        }
+        case IKBO_PROBE_READ: {
+            // reads all of buf but the last blocks * 256 words, which receive the per-thread results
+            if (bytes <= per_thread_out + 16 || ((uintptr_t)buf & 15)) return 1;
+            const int64_t n16 = (int64_t)((bytes - per_thread_out) / 16);
+            hipLaunchKernelGGL(probe_read_kernel, grid, block, 0, s, (const uint4 *)buf, n16,
+                               (uint32_t *)((char *)buf + (size_t)n16 * 16));
+            break;
+        }
+        default:
+            return 1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+}  // extern "C"

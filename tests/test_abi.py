@@ -251,3 +251,22 @@ def test_lcb_emb_argument_errors(lib):
     assert lcbe(lib, ws=None) == ikbo.IKBO_WORKSPACE_TOO_SMALL
     assert lcbe(lib, C=0, yr=None) == ikbo.IKBO_OK        # nothing to compute
     assert lcbe(lib, kc=0, yr=None, ws=None, wsb=0) == ikbo.IKBO_OK
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The ceiling probes (include/ikbo_probe.h) load, export their one entry point, and refuse bad
+    arguments before launching anything."""
+    probe_h = os.path.join(os.path.dirname(HEADER), "ikbo_probe.h")
+    names = set(re.findall(r"^\s*int\s+(ikbo_probe_[a-z_]+)\s*\(", open(probe_h).read(), re.M))
+    assert names == {"ikbo_probe_launch"}
+    if not os.path.exists(ikbo.PROBE_PATH):
+        from request_candidate_broadcast_amd import _build
+        _build.build_probe(verbose=False)
+    out = subprocess.run(["nm", "-D", "--defined-only", ikbo.PROBE_PATH], stdout=subprocess.PIPE, text=True).stdout
+    assert re.search(r"\bT ikbo_probe_launch\b", out)
+    lib = ikbo.load_probe()
+    assert lib.ikbo_probe_launch(0, None, 1 << 20, 10, 4, None) == 1          # NULL buffer
+    assert lib.ikbo_probe_launch(0, FAKE, 1 << 20, 10, 0, None) == 1          # no blocks
+    assert lib.ikbo_probe_launch(0, FAKE, 1000, 10, 4, None) == 1             # output too small
+    assert lib.ikbo_probe_launch(9, FAKE, 1 << 20, 10, 4, None) == 1          # unknown probe
+    assert lib.ikbo_probe_launch(2, FAKE + 4, 1 << 20, 0, 4, None) == 1       # misaligned copy
