@@ -146,10 +146,11 @@ __device__ __forceinline__ void exp_block(f32x16 &s, bf16x8 (&pb)[2], float &l, 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[u][e] = (__bf16)s[8 * u + e];
-#pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pr = {pb[u][e], pb[u][e + 1]};
+            // a pair at a time: one v_cvt_pk_bf16_f32 per two weights
+            const bf16x2 pr = cvt_bf16x2(s[8 * u + e], s[8 * u + e + 1]);
+            pb[u][e] = pr[0];
+            pb[u][e + 1] = pr[1];
             l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
         }
     }

@@ -27,8 +27,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two values at once: one v_cvt_pk_bf16_f32 (the same rounding as f32_to_bf16 on each).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2_t cvt_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_convertvector(v, bf16x2_t);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, cvt_bf16x2(lo, hi));
 }
 
 // GELU, exact form x Phi(x) = x/2 (1 + erf(x / sqrt 2)), with erf from the rational approximation of
