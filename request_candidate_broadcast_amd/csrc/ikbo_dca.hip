@@ -157,7 +157,7 @@ __device__ __forceinline__ void exp_block(f32x16 &s, bf16x8 (&pb)[2], float &l, 
 }
 
 template <int D, int NW, int NKB, int NBUF, int KPD, int VPD, int COPYAT>
-__global__ __launch_bounds__(NW * 64) void dca_bf16_kernel(DcaArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1, 8))) void dca_bf16_kernel(DcaArgs a) {
     constexpr int BN = NKB * 32;                       // keys per tile
     constexpr int BM = NW * 32;                        // stacked query rows per workgroup
     constexpr int CPR = D / 8;                         // 16-byte chunks per key row
