@@ -218,8 +218,8 @@ struct NoHook {
 // after the loads of its first column group are issued (LDS is free by then: a copy issued there
 // does not delay those loads, which it would when issued before them). prefetched: the caller has
 // already copied step 0 into stage 0 with dma_fetch (direct copies, two stages).
-template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL, bool ZCOH, typename Pre,
-          typename Mid = NoHook>
+template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL, bool ZCOH, bool STG,
+          typename Pre, typename Mid = NoHook>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int sp, int32_t k_per_split,
                                           uint4 *const *sx, uint4 *const *sw, Pre pre_epilogue,
                                           bool prefetched = false, Mid mid_epilogue = Mid()) {
@@ -444,6 +444,37 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
                 ob[j] = (char *)a.out + (rowj[j] * a.ldo + cw + 4 * half) * osz;
             }
             const float *bb = a.bias ? a.bias + cw + 4 * half : nullptr;
+            // Staged stores. A lane holds 4-column pieces of one row, so a direct store puts 8 or 16
+            // bytes into each of 32 rows. Instead the wave's results for 128 output bytes of each of
+            // its rows (two 32-column groups in bf16, one in fp32) go to a per-wave area of LDS stage
+            // 1, which is free once the main loop has ended (with two stages its last copy lands in
+            // stage 0, and a persistent caller prefetches only into stage 0), and leave as whole
+            // 128-byte row pieces, 8 rows per store. 16-byte chunks are XOR-swizzled by row & 7.
+            constexpr int NW2 = WGM * WGN / 2;
+            static_assert(NBUF == 2 && WGM * WGN % 2 == 0 && NW2 * TM * 8 <= XCH && NW2 * TM * 8 <= WCH,
+                          "output staging: each wave's TM x 128-byte area must fit in LDS stage 1");
+            char *const stg = (char *)(wave < NW2 ? sx[1] + wave * TM * 8 : sw[1] + (wave - NW2) * TM * 8);
+            // addresses: a wave-uniform base (SGPRs) plus one 32-bit lane offset
+            const int srow = lane >> 3, sch = lane & 7;
+            const int64_t wrow0 = m0 + wm * TM;
+            const int64_t obase_el = wrow0 * a.ldo + cw;
+            char *const obase = (char *)a.out +
+                                (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(obase_el >> 32)) << 32) |
+                                          (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)obase_el)) * osz;
+            const uint32_t loff = (uint32_t)(srow * a.ldo * osz) + sch * 16;
+            const int64_t ostep = 8 * a.ldo * osz;
+            const int rows_here = (int)min((int64_t)TM, a.M - wrow0) - srow;     // this lane's rows: srow + 8k
+            auto flush = [&](int col_bytes) __attribute__((always_inline)) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave's LDS writes first
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int k = 0; k < TM / 8; ++k) {
+                    const uint4 val = *(const uint4 *)(stg + (srow + 8 * k) * 128 + (sch ^ srow) * 16);
+                    if (8 * k < rows_here) *(uint4 *)(obase + k * ostep + col_bytes + loff) = val;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // reads before the next writes
+                __builtin_amdgcn_wave_barrier();
+            };
             auto body = [&](auto HB, auto HZ, auto HC) __attribute__((always_inline)) {
                 static_for<NB>([&](auto I) __attribute__((always_inline)) {
                     constexpr int i = decltype(I)::value;
@@ -492,7 +523,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
 #pragma unroll
                             for (int e = 0; e < 16; ++e) v[j][e] = rok[j] ? v[j][e] : 0.0f;
                     }
-                    if (a.out_f32) {
+                    if constexpr (STG) {
+                        const int sw7 = l32 & 7;
+                        if (a.out_f32) {
+#pragma unroll
+                            for (int j = 0; j < MB; ++j)
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj)
+                                    *(float4 *)(stg + (j * 32 + l32) * 128 + ((2 * jj + half) ^ sw7) * 16) =
+                                        make_float4(v[j][4 * jj], v[j][4 * jj + 1], v[j][4 * jj + 2], v[j][4 * jj + 3]);
+                            flush(i * 128);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < MB; ++j)
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj)
+                                    *(uint2 *)(stg + (j * 32 + l32) * 128 + (((i & 1) * 4 + jj) ^ sw7) * 16 + 8 * half) =
+                                        make_uint2(pack_bf16x2(v[j][4 * jj], v[j][4 * jj + 1]),
+                                                   pack_bf16x2(v[j][4 * jj + 2], v[j][4 * jj + 3]));
+                            if constexpr ((i & 1) == 1 || i == NB - 1) flush((i >> 1) * 128);
+                        }
+                    } else if (a.out_f32) {
 #pragma unroll
                         for (int j = 0; j < MB; ++j)
                             if (rin[j])
@@ -565,7 +616,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
     uint4 *const sx[4] = {sx0, sx1, sx2, sx3};                                                                      \
     uint4 *const sw[4] = {sw0, sw1, sw2, sw3}
 
-template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL>
+template <int WGM, int WGN, int TM, int TN, int TBK, int NBUF, bool DMA, bool PARTIAL, bool STG>
 __global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t tiles_m, int32_t tiles_n,
                                                             int32_t k_per_split) {
     using G = GemmShape<WGM, WGN, TM, TN, TBK>;
@@ -577,7 +628,7 @@ __global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t
     t /= tiles_n;
     const int mt = (int)(t % tiles_m);
     const int sp = (int)(t / tiles_m);
-    gemm_tile<WGM, WGN, TM, TN, TBK, NBUF, DMA, PARTIAL, false>(a, mt, nt, sp, k_per_split, sx, sw, [] {});
+    gemm_tile<WGM, WGN, TM, TN, TBK, NBUF, DMA, PARTIAL, false, STG>(a, mt, nt, sp, k_per_split, sx, sw, [] {});
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -764,7 +815,7 @@ __device__ __forceinline__ int32_t lane0(int lane, Op op) {
     return __builtin_amdgcn_readfirstlane(v);
 }
 
-template <bool DMA_R, bool DMA_C>
+template <bool DMA_R, bool DMA_C, bool STG>
 __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f) {
     using G = GemmShape<kWGM, kWGN, kTM, kTN, BK>;
     IKBO_GEMM_LDS(G, 2);
@@ -815,7 +866,7 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
             const int64_t tile = item / splits;
             const int sp = (int)(item % splits);
             const int mt = (int)(tile / rtn), nt = (int)(tile % rtn);
-            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_R, true, false>(rq, mt, nt, sp, rkps, sx, sw, [] {});
+            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_R, true, false, false>(rq, mt, nt, sp, rkps, sx, sw, [] {});
             // every wave's partial stores have reached the L2; one release (an L2 write-back) by
             // wave 0 then puts them in memory before the arrival is counted
             wait_vmcnt<0>();
@@ -909,7 +960,7 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
             // the epilogue reads Z with plain loads when its lines hold one request tile each, else
             // with coherent loads; no acquire fence, which would invalidate the XCD's L2 (and the
             // weight and activation tiles the other workgroups there hold) per tile
-            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_C, false, true>(cd, mt, nt, 0, cd.K, sx, sw, pre, prefetched, mid);
+            gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_C, false, true, STG>(cd, mt, nt, 0, cd.K, sx, sw, pre, prefetched, mid);
             if (!__builtin_amdgcn_readfirstlane(s_flag)) {
                 // the wait ran out: mark the tile's rows as invalid output
                 for (int i = tid; i < BM * BN; i += kGemmThreads) {
@@ -949,6 +1000,11 @@ static bool gemm_dma_ok(const GemmArgs &a, int32_t kps) {
            (int64_t)BM * a.ldx * 2 < (1LL << 31) && (int64_t)BN * a.K * 2 < (1LL << 31);
 }
 
+// the staged epilogue stores 16-byte pieces of output rows: 16-byte aligned output and rows
+static bool out_staging_ok(const GemmArgs &a) {
+    return ((uintptr_t)a.out & 15) == 0 && (a.out_f32 || (a.ldo & 7) == 0);
+}
+
 static int32_t k_per_split(const GemmArgs &a) {
     const int splits = a.partial ? (a.splits > 0 ? a.splits : 1) : 1;
     int32_t kps = (int32_t)((((int64_t)a.K + splits - 1) / splits + BK - 1) / BK * BK);
@@ -974,15 +1030,18 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
         // direct copies: k tiles whole, 16-byte aligned rows, buffer ranges within 32 bits, and no
         // tile across the w0 / w1 boundary
         const bool dma = gemm_dma_ok(a, kps);
-#define IKBO_GEMM(D, P)                                                                                              \
-    hipLaunchKernelGGL((gemm_bf16_t<kWGM, kWGN, kTM, kTN, BK, 2, D, P>), dim3((unsigned)grid), dim3(kGemmThreads), 0, \
-                       s, b, (int32_t)tm, (int32_t)tn, kps)
+#define IKBO_GEMM(D, P, S)                                                                                           \
+    hipLaunchKernelGGL((gemm_bf16_t<kWGM, kWGN, kTM, kTN, BK, 2, D, P, S>), dim3((unsigned)grid), dim3(kGemmThreads),   \
+                       0, s, b, (int32_t)tm, (int32_t)tn, kps)
+        const bool stg = out_staging_ok(a);
         if (dma) {
-            if (a.partial) IKBO_GEMM(true, true);
-            else IKBO_GEMM(true, false);
+            if (a.partial) IKBO_GEMM(true, true, false);
+            else if (stg) IKBO_GEMM(true, false, true);
+            else IKBO_GEMM(true, false, false);
         } else {
-            if (a.partial) IKBO_GEMM(false, true);
-            else IKBO_GEMM(false, false);
+            if (a.partial) IKBO_GEMM(false, true, false);
+            else if (stg) IKBO_GEMM(false, false, true);
+            else IKBO_GEMM(false, false, false);
         }
 #undef IKBO_GEMM
     }
@@ -1026,7 +1085,8 @@ hipError_t launch_lcb_fused(const LcbFusedArgs &f, hipStream_t s) {
                           ((f.cand.M + BM - 1) / BM) * ((f.cand.N + BN - 1) / BN);
     int64_t grid = min((int64_t)cus, items);
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
-    hipLaunchKernelGGL((lcb_fused_kernel<true, true>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, f);
+    if (out_staging_ok(f.cand)) hipLaunchKernelGGL((lcb_fused_kernel<true, true, true>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, f);
+    else hipLaunchKernelGGL((lcb_fused_kernel<true, true, false>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, f);
     return hipGetLastError();
 }
 
