@@ -61,9 +61,10 @@ def test_tiny_fp32_workload():
 
 @pytest.mark.parametrize("act", ["gelu", "none"])
 # (k_req, k_cand, n_req, n_cand): k tails, tiny K, long split-K request GEMM, and with K a
-# multiple of 64 (direct LDS copies) ragged N over several column tiles
+# multiple of 64 (direct LDS copies) ragged N over several column tiles; N = 300 has a whole
+# column tile with bf16 rows of 600 bytes (direct stores) and fp32 rows of 1200 (staged stores)
 @pytest.mark.parametrize("shape", [(136, 264, 72, 200), (64, 8, 40, 203), (4096, 512, 256, 256),
-                                   (128, 192, 256, 200), (64, 256, 520, 1000)])
+                                   (128, 192, 256, 200), (64, 256, 520, 1000), (64, 128, 40, 300)])
 def test_bf16_ragged_shapes(act, shape):
     k_req, k_cand, n_req, n_cand = shape
     counts = np.array([1, 300, 0, 77, 513, 2, 40])
