@@ -78,6 +78,9 @@ def parse():
                                                            "stack"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA / HBM / exp2 ceilings")
+    p.add_argument("--flush-mib", type=int, default=512,
+                   help="cold-cache pass after the timed steps: this many MiB written between steps, outside "
+                        "their events, so no input stays in L2 or the 256 MiB MALL (0 = skip the pass)")
     p.add_argument("--cpu-sample", type=int, default=0, help="candidates in the oracle sample (0 = default)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="per-kernel HBM bytes measured with rocprofv3 counters, if present")
@@ -388,10 +391,30 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     log("timed %d steps: %.3f ms/step" % (args.steps, ms_step))
 
+    # cold-cache pass: the same steps, each after a write of flush-mib MiB on the same stream that
+    # evicts the previous step's data from L2 and the MALL (outside the events, not in ms_per_step)
+    cold = None
+    if args.flush_mib > 0:
+        fbuf = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                fbuf.fill_(i & 0xff)
+                step(cev[i])
+        torch.cuda.synchronize()
+        del fbuf
+        cold = {"flush_mib": args.flush_mib}
+        for name, a, b in names:
+            d = [cev[i][a].elapsed_time(cev[i][b]) for i in range(args.steps)]
+            cold[name] = {"ms_median": float(np.median(d)), "ms_min": float(np.min(d)),
+                          "ms_p90": float(np.percentile(d, 90))}
+        log("cold-cache pass done")
+
     per = {}
     for name, a, b in names:
         d = [timed[i][a].elapsed_time(timed[i][b]) for i in range(args.steps)]
-        per[name] = {"ms_avg": float(np.mean(d)), "ms_min": float(np.min(d)), "ms_median": float(np.median(d))}
+        per[name] = {"ms_avg": float(np.mean(d)), "ms_min": float(np.min(d)), "ms_median": float(np.median(d)),
+                     "ms_p90": float(np.percentile(d, 90))}
         per[name]["tflops"] = flops[name] / (per[name]["ms_avg"] * 1e-3) / 1e12
         per[name]["gbs_algorithmic"] = algo_bytes[name] / (per[name]["ms_avg"] * 1e-3) / 1e9
         per[name]["mfma_frac"] = per[name]["tflops"] / PEAK_BF16_TFLOPS
@@ -474,6 +497,9 @@ def main():
     }
     if alt:
         line["alternate_forms"] = alt
+    if cold:
+        line["cold_l2"] = {k: ({kk: round(vv, 4) for kk, vv in d.items()} if isinstance(d, dict) else d)
+                           for k, d in cold.items()}
     print(json.dumps(line), flush=True)
 
 
