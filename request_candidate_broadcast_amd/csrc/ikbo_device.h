@@ -27,6 +27,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// 16-byte store with the non-temporal hint, for streamed outputs written in whole 128-byte lines
+// (8 lanes per line): the lines go out without displacing operand tiles that other workgroups
+// still read from L2. Stores that cover only part of a line are slower with the hint (the L2 no
+// longer merges them), so they keep plain stores.
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt16(void *p, uint4 v) {
+    const nt_u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (nt_u32x4 *)p);
+}
+
 // Two values at once: one v_cvt_pk_bf16_f32 (the same rounding as f32_to_bf16 on each).
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

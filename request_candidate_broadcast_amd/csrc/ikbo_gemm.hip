@@ -449,7 +449,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
             // its rows (two 32-column groups in bf16, one in fp32) go to a per-wave area of LDS stage
             // 1, which is free once the main loop has ended (with two stages its last copy lands in
             // stage 0, and a persistent caller prefetches only into stage 0), and leave as whole
-            // 128-byte row pieces, 8 rows per store. 16-byte chunks are XOR-swizzled by row & 7.
+            // 128-byte row pieces, 8 rows per store (non-temporal: the output is streamed). 16-byte
+            // chunks are XOR-swizzled by row & 7.
             constexpr int NW2 = WGM * WGN / 2;
             static_assert(NBUF == 2 && WGM * WGN % 2 == 0 && NW2 * TM * 8 <= XCH && NW2 * TM * 8 <= WCH,
                           "output staging: each wave's TM x 128-byte area must fit in LDS stage 1");
@@ -470,7 +471,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
 #pragma unroll
                 for (int k = 0; k < TM / 8; ++k) {
                     const uint4 val = *(const uint4 *)(stg + (srow + 8 * k) * 128 + (sch ^ srow) * 16);
-                    if (8 * k < rows_here) *(uint4 *)(obase + k * ostep + col_bytes + loff) = val;
+                    if (8 * k < rows_here) store_nt16(obase + k * ostep + col_bytes + loff, val);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // reads before the next writes
                 __builtin_amdgcn_wave_barrier();
