@@ -65,7 +65,7 @@ __device__ __forceinline__ void fm_flush(const float *st, int SW, void *y, int o
         const int cpr = W / 4;
         for (int i = lane; i < nrows * cpr; i += 64) {
             const int row = i / cpr, q = i - row * cpr;
-            *(float4 *)((float *)y + base + (int64_t)row * W + 4 * q) = *(const float4 *)(st + row * SW + 4 * q);
+            store_nt16((float *)y + base + (int64_t)row * W + 4 * q, *(const uint4 *)(st + row * SW + 4 * q));
         }
     } else if (W % 8 == 0) {
         const int cpr = W / 8;
@@ -73,8 +73,8 @@ __device__ __forceinline__ void fm_flush(const float *st, int SW, void *y, int o
             const int row = i / cpr, q = i - row * cpr;
             const float4 u = *(const float4 *)(st + row * SW + 8 * q);
             const float4 v = *(const float4 *)(st + row * SW + 8 * q + 4);
-            *(uint4 *)((uint16_t *)y + base + (int64_t)row * W + 8 * q) =
-                make_uint4(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+            store_nt16((uint16_t *)y + base + (int64_t)row * W + 8 * q,
+                       make_uint4(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)));
         }
     } else {
         const int cpr = W / 4;

@@ -392,9 +392,9 @@ __global__ __launch_bounds__(kLeWaves * 64) __attribute__((amdgpu_waves_per_eu(W
                     yp[0] = make_float4(o8[0], o8[1], o8[2], o8[3]);
                     yp[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
                 } else {
-                    *(uint4 *)((uint16_t *)a.y_c + yo) =
-                        make_uint4(pack_bf16x2(o8[0], o8[1]), pack_bf16x2(o8[2], o8[3]), pack_bf16x2(o8[4], o8[5]),
-                                   pack_bf16x2(o8[6], o8[7]));
+                    store_nt16((uint16_t *)a.y_c + yo,
+                               make_uint4(pack_bf16x2(o8[0], o8[1]), pack_bf16x2(o8[2], o8[3]), pack_bf16x2(o8[4], o8[5]),
+                                          pack_bf16x2(o8[6], o8[7])));
                 }
             }
             wave_lds_fence();
