@@ -322,6 +322,9 @@ static int dca_run(const void *q, int64_t C, int32_t q_len, const void *k, const
     const int64_t row_elems = (int64_t)q_len * num_heads * head_dim;
     if (q_cs == 0) q_cs = row_elems;
     if (o_cs == 0) o_cs = row_elems;
+    // the bf16 kernel reads and writes rows in 16-byte pieces
+    if (!in_f32 && (q_cs % 8 != 0 || o_cs % 8 != 0))
+        return fail(IKBO_MISALIGNED, "candidate row strides must be multiples of 8 elements");
     const int ob = (int)esize(out_dtype);
     // few stacked query rows per request (at most 32 on average): one-wave, 32-row work tiles
     // work tile by the average stacked query rows per request: at most 32 one wave, at most 1024

@@ -445,22 +445,52 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
 
     // ---- epilogue: O = O^T / l ----
     const float l_tot = half_swap_sum(l);
-    if (!rvalid) return;
     const float inv = !fits ? __builtin_nanf("") : l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const int64_t obase = cand * a.o_cs + tok * HD + ti.h * D;
+    if (a.out_f32) {
+        if (!rvalid) return;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d = db * 32 + 8 * jj + 4 * half;
+                *(float4 *)((float *)a.out + obase + d) = make_float4(o[db][4 * jj] * inv, o[db][4 * jj + 1] * inv,
+                                                                      o[db][4 * jj + 2] * inv, o[db][4 * jj + 3] * inv);
+            }
+        return;
+    }
+    // bf16: a lane holds 4-dim pieces of its row, so direct stores would put 8 bytes into each of
+    // 32 rows. The wave's 32 rows (2D bytes each) go through its own area of the K/V stages, idle
+    // since the last barrier, and leave as whole rows, CPR lanes per row. The 16-byte chunks are
+    // XOR-swizzled so that both the 32-row writes and the whole-row reads spread over all banks.
+    // Rows start on 16 bytes: the host checks the base and a candidate stride of 8k elements.
+    constexpr int RPI = 64 / CPR;                       // rows per store instruction
+    static_assert(NW <= 8 && 64 * CPR <= kInstrK * 64 && 64 * CPR <= kInstrV * 64, "O staging: two waves per stage buffer");
+    const int sbuf = wave >> 1;
+    uint4 *const stg = (sbuf == 0 ? k_s0 : sbuf == 1 ? k_s1 : sbuf == 2 ? v_s0 : v_s1) + (wave & 1) * 32 * CPR;
+    auto swz = [](int r) __attribute__((always_inline)) { return CPR >= 16 ? (r & 15) : ((r >> 1) & 7); };
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int d = db * 32 + 8 * jj + 4 * half;
             const float v0 = o[db][4 * jj + 0] * inv, v1 = o[db][4 * jj + 1] * inv;
             const float v2 = o[db][4 * jj + 2] * inv, v3 = o[db][4 * jj + 3] * inv;
-            if (a.out_f32) {
-                *(float4 *)((float *)a.out + obase + d) = make_float4(v0, v1, v2, v3);
-            } else {
-                *(uint2 *)((uint16_t *)a.out + obase + d) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-            }
+            *(uint2 *)((char *)(stg + l32 * CPR + ((db * 4 + jj) ^ swz(l32))) + 8 * half) =
+                make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
         }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave's LDS writes first
+    __builtin_amdgcn_wave_barrier();
+    const int64_t omark = rvalid ? obase : -1;               // row r's lanes are r and r + 32
+    const int fr = lane / CPR, fc = lane % CPR;
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+        const int r = fr + k * RPI;
+        const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)omark, r);
+        const int32_t hi = __shfl((int)(omark >> 32), r);
+        const int64_t ob = (int64_t)(((uint64_t)(uint32_t)hi << 32) | lo);
+        const uint4 val = stg[r * CPR + (fc ^ swz(r))];
+        if (ob >= 0) *(uint4 *)((uint16_t *)a.out + ob + fc * 8) = val;
+    }
 }
 
 // The configurations the library launches, per head dim: 8 waves x 32 query rows, 64-key tiles,
