@@ -461,8 +461,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     }
     // bf16: a lane holds 4-dim pieces of its row, so direct stores would put 8 bytes into each of
     // 32 rows. The wave's 32 rows (2D bytes each) go through its own area of the K/V stages, idle
-    // since the last barrier, and leave as whole rows, CPR lanes per row. The 16-byte chunks are
-    // XOR-swizzled so that both the 32-row writes and the whole-row reads spread over all banks.
+    // since the last barrier, and leave as whole rows, CPR lanes per row, with the non-temporal
+    // hint (whole lines). The 16-byte chunks are XOR-swizzled so that both the 32-row writes and
+    // the whole-row reads spread over all banks.
     // Rows start on 16 bytes: the host checks the base and a candidate stride of 8k elements.
     constexpr int RPI = 64 / CPR;                       // rows per store instruction
     static_assert(NW <= 8 && 64 * CPR <= kInstrK * 64 && 64 * CPR <= kInstrV * 64, "O staging: two waves per stage buffer");
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
         const int32_t hi = __shfl((int)(omark >> 32), r);
         const int64_t ob = (int64_t)(((uint64_t)(uint32_t)hi << 32) | lo);
         const uint4 val = stg[r * CPR + (fc ^ swz(r))];
-        if (ob >= 0) *(uint4 *)((uint16_t *)a.out + ob + fc * 8) = val;
+        if (ob >= 0) store_nt16((uint16_t *)a.out + ob + fc * 8, val);
     }
 }
 
