@@ -462,8 +462,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     // bf16: a lane holds 4-dim pieces of its row, so direct stores would put 8 bytes into each of
     // 32 rows. The wave's 32 rows (2D bytes each) go through its own area of the K/V stages, idle
     // since the last barrier, and leave as whole rows, CPR lanes per row, with the non-temporal
-    // hint (whole lines). The 16-byte chunks are XOR-swizzled so that both the 32-row writes and
-    // the whole-row reads spread over all banks.
+    // hint (whole lines). The 16-byte chunks are XOR-swizzled, and rows 16-31 hold the two 8-byte
+    // halves of each chunk swapped, so that both the 32-row writes and the whole-row reads are
+    // free of bank conflicts.
     // Rows start on 16 bytes: the host checks the base and a candidate stride of 8k elements.
     constexpr int RPI = 64 / CPR;                       // rows per store instruction
     static_assert(NW <= 8 && 64 * CPR <= kInstrK * 64 && 64 * CPR <= kInstrV * 64, "O staging: two waves per stage buffer");
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
         for (int jj = 0; jj < 4; ++jj) {
             const float v0 = o[db][4 * jj + 0] * inv, v1 = o[db][4 * jj + 1] * inv;
             const float v2 = o[db][4 * jj + 2] * inv, v3 = o[db][4 * jj + 3] * inv;
-            *(uint2 *)((char *)(stg + l32 * CPR + ((db * 4 + jj) ^ swz(l32))) + 8 * half) =
+            *(uint2 *)((char *)(stg + l32 * CPR + ((db * 4 + jj) ^ swz(l32))) + 8 * (half ^ (l32 >> 4))) =
                 make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
         }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave's LDS writes first
@@ -489,7 +490,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
         const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)omark, r);
         const int32_t hi = __shfl((int)(omark >> 32), r);
         const int64_t ob = (int64_t)(((uint64_t)(uint32_t)hi << 32) | lo);
-        const uint4 val = stg[r * CPR + (fc ^ swz(r))];
+        uint4 val = stg[r * CPR + (fc ^ swz(r))];
+        if ((r >> 4) & 1) val = make_uint4(val.z, val.w, val.x, val.y);
         if (ob >= 0) store_nt16((uint16_t *)a.out + ob + fc * 8, val);
     }
 }

@@ -450,7 +450,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
             // 1, which is free once the main loop has ended (with two stages its last copy lands in
             // stage 0, and a persistent caller prefetches only into stage 0), and leave as whole
             // 128-byte row pieces, 8 rows per store (non-temporal: the output is streamed). 16-byte
-            // chunks are XOR-swizzled by row & 7.
+            // chunks are XOR-swizzled by (row >> 1) & 7, and in bf16 rows 16-31 of a 32-row block
+            // hold the two 8-byte halves of each chunk swapped, so the 32-row writes and the
+            // whole-row reads are free of bank conflicts.
             constexpr int NW2 = WGM * WGN / 2;
             static_assert(NBUF == 2 && WGM * WGN % 2 == 0 && NW2 * TM * 8 <= XCH && NW2 * TM * 8 <= WCH,
                           "output staging: each wave's TM x 128-byte area must fit in LDS stage 1");
@@ -465,12 +467,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
             const uint32_t loff = (uint32_t)(srow * a.ldo * osz) + sch * 16;
             const int64_t ostep = 8 * a.ldo * osz;
             const int rows_here = (int)min((int64_t)TM, a.M - wrow0) - srow;     // this lane's rows: srow + 8k
-            auto flush = [&](int col_bytes) __attribute__((always_inline)) {
+            auto flush = [&](int col_bytes, bool swapped) __attribute__((always_inline)) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave's LDS writes first
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
                 for (int k = 0; k < TM / 8; ++k) {
-                    const uint4 val = *(const uint4 *)(stg + (srow + 8 * k) * 128 + (sch ^ srow) * 16);
+                    const int row = srow + 8 * k;
+                    uint4 val = *(const uint4 *)(stg + row * 128 + (sch ^ ((row >> 1) & 7)) * 16);
+                    if (swapped && ((row >> 4) & 1)) val = make_uint4(val.z, val.w, val.x, val.y);
                     if (8 * k < rows_here) store_nt16(obase + k * ostep + col_bytes + loff, val);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // reads before the next writes
@@ -525,7 +529,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
                             for (int e = 0; e < 16; ++e) v[j][e] = rok[j] ? v[j][e] : 0.0f;
                     }
                     if constexpr (STG) {
-                        const int sw7 = l32 & 7;
+                        const int sw7 = (l32 >> 1) & 7, hs = half ^ ((l32 >> 4) & 1);
                         if (a.out_f32) {
 #pragma unroll
                             for (int j = 0; j < MB; ++j)
@@ -533,16 +537,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
                                 for (int jj = 0; jj < 4; ++jj)
                                     *(float4 *)(stg + (j * 32 + l32) * 128 + ((2 * jj + half) ^ sw7) * 16) =
                                         make_float4(v[j][4 * jj], v[j][4 * jj + 1], v[j][4 * jj + 2], v[j][4 * jj + 3]);
-                            flush(i * 128);
+                            flush(i * 128, false);
                         } else {
 #pragma unroll
                             for (int j = 0; j < MB; ++j)
 #pragma unroll
                                 for (int jj = 0; jj < 4; ++jj)
-                                    *(uint2 *)(stg + (j * 32 + l32) * 128 + (((i & 1) * 4 + jj) ^ sw7) * 16 + 8 * half) =
+                                    *(uint2 *)(stg + (j * 32 + l32) * 128 + (((i & 1) * 4 + jj) ^ sw7) * 16 + 8 * hs) =
                                         make_uint2(pack_bf16x2(v[j][4 * jj], v[j][4 * jj + 1]),
                                                    pack_bf16x2(v[j][4 * jj + 2], v[j][4 * jj + 3]));
-                            if constexpr ((i & 1) == 1 || i == NB - 1) flush((i >> 1) * 128);
+                            if constexpr ((i & 1) == 1 || i == NB - 1) flush((i >> 1) * 128, true);
                         }
                     } else if (a.out_f32) {
 #pragma unroll
