@@ -463,8 +463,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     // 32 rows. The wave's 32 rows (2D bytes each) go through its own area of the K/V stages, idle
     // since the last barrier, and leave as whole rows, CPR lanes per row, with the non-temporal
     // hint (whole lines). The 16-byte chunks are XOR-swizzled, and rows 16-31 hold the two 8-byte
-    // halves of each chunk swapped, so that both the 32-row writes and the whole-row reads are
-    // free of bank conflicts.
+    // halves of each chunk swapped, so that no two rows of a 32-lane write, and no two chunks of a
+    // whole-row read, fall on the same banks.
     // Rows start on 16 bytes: the host checks the base and a candidate stride of 8k elements.
     constexpr int RPI = 64 / CPR;                       // rows per store instruction
     static_assert(NW <= 8 && 64 * CPR <= kInstrK * 64 && 64 * CPR <= kInstrV * 64, "O staging: two waves per stage buffer");

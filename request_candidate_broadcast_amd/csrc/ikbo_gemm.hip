@@ -451,8 +451,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
             // stage 0, and a persistent caller prefetches only into stage 0), and leave as whole
             // 128-byte row pieces, 8 rows per store (non-temporal: the output is streamed). 16-byte
             // chunks are XOR-swizzled by (row >> 1) & 7, and in bf16 rows 16-31 of a 32-row block
-            // hold the two 8-byte halves of each chunk swapped, so the 32-row writes and the
-            // whole-row reads are free of bank conflicts.
+            // hold the two 8-byte halves of each chunk swapped, so no two rows of a 32-lane write,
+            // and no two chunks of a whole-row read, fall on the same banks.
             constexpr int NW2 = WGM * WGN / 2;
             static_assert(NBUF == 2 && WGM * WGN % 2 == 0 && NW2 * TM * 8 <= XCH && NW2 * TM * 8 <= WCH,
                           "output staging: each wave's TM x 128-byte area must fit in LDS stage 1");
