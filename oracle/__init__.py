@@ -78,7 +78,7 @@ def _get():
         lib.oracle_gelu.restype = dbl
         lib.oracle_gelu.argtypes = [dbl]
         lib.oracle_request_of.restype = i64
-        lib.oracle_request_of.argtypes = [vp, vp, i64, i64]
+        lib.oracle_request_of.argtypes = [vp, vp, i64, i64, vp]
         lib.oracle_dca.restype = ctypes.c_int
         lib.oracle_dca.argtypes = [vp, i64, i32, vp, vp, i64, vp, i32, vp, vp, i32, i32, dbl, i32, i32,
                                    vp, i64, vp, ctypes.POINTER(ctypes.c_int64), i32]
@@ -120,8 +120,11 @@ def gelu(x: float) -> float:
 
 
 def request_of(m, off, R: int, c: int) -> int:
+    """Request of candidate c: from the offsets when given (they define the grouping), else from
+    the map; -1 when it has none. A map that disagrees with the offsets is a violation (see
+    ``index_violations``), not an error."""
     m, off = _i32(m), _i32(off)
-    return int(_get().oracle_request_of(_ptr(m), _ptr(off), R, c))
+    return int(_get().oracle_request_of(_ptr(m), _ptr(off), R, c, None))
 
 
 def dca(q: np.ndarray, k: np.ndarray, v: np.ndarray, R: int, *, m=None, off=None, kv_cu=None,
@@ -251,7 +254,7 @@ def fm(x_r: np.ndarray, x_c: np.ndarray, *, m=None, off=None, cands: Optional[Se
     y_c = np.zeros((len(ids), n_c, n_r + n_c), dtype=np.float64)
     mm, oo = _i32(m), _i32(off)
     for o, c in enumerate(ids):
-        r = int(_get().oracle_request_of(_ptr(mm), _ptr(oo), R, int(c)))
+        r = int(_get().oracle_request_of(_ptr(mm), _ptr(oo), R, int(c), None))
         if r < 0:
             continue
         y_c[o, :, :n_r] = xc[c] @ xr[r].T          # request-candidate interactions (the broadcast term)
@@ -329,7 +332,7 @@ def lcb_emb(x_r: np.ndarray, x_c: np.ndarray, w_rr: np.ndarray, w_cr: np.ndarray
     R = xr.shape[0]
     ids = np.arange(xc.shape[0]) if cands is None else np.asarray(cands, dtype=np.int64)
     mm, oo = _i32(m), _i32(off)
-    req = np.array([_get().oracle_request_of(_ptr(mm), _ptr(oo), R, int(c)) for c in ids], dtype=np.int64)
+    req = np.array([_get().oracle_request_of(_ptr(mm), _ptr(oo), R, int(c), None) for c in ids], dtype=np.int64)
     y_c = np.zeros((len(ids), wcc.shape[0], xc.shape[2]), dtype=np.float64)
     for s in range(0, len(ids), chunk):
         sl = slice(s, s + chunk)
@@ -347,5 +350,9 @@ def lcb_emb(x_r: np.ndarray, x_c: np.ndarray, w_rr: np.ndarray, w_cr: np.ndarray
 
 
 def index_violations(m, off, C: int, R: int, sorted_flag: bool = False) -> int:
+    """Faults of an index, each counted once: with offsets, off[0] != 0 and off[R] != C (one each)
+    and every decreasing step; with a map, every entry outside [0, R), with sorted_flag every entry
+    below its predecessor, and with both, every valid entry whose candidate lies outside its
+    request's offset range."""
     m, off = _i32(m), _i32(off)
     return int(_get().oracle_index_violations(_ptr(m), _ptr(off), C, R, 1 if sorted_flag else 0))

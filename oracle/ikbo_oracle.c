@@ -19,8 +19,10 @@
  * Conventions (the pages give none; these are the readings used throughout):
  *  - Q and O are [C, Lq, H, d]; K and V are [R, L, H, d] (uniform length) or [sum L_r, H, d]
  *    with prefix offsets kv_cu [R+1] (variable length); weights are [N_out, K_in] (y = W x).
- *  - The request of candidate c is m[c] when m is given, else the r with off[r] <= c < off[r+1].
- *    If both are given and disagree the call fails. A request index outside [0, R) gives an
+ *  - The request of candidate c is the r with off[r] <= c < off[r+1] when the offsets are given
+ *    (they are the contiguous grouping of Sec. 4.2.1), else m[c]. When both are given they must
+ *    agree; a candidate whose m[c] names another request is counted as a violation and still
+ *    takes its request from the offsets. A candidate with no request in [0, R) gives an
  *    all-zero output row and is counted as a violation.
  *  - Softmax is over all L_r keys of the candidate's request; no masking.
  *  - GELU is the exact erf form x * Phi(x), using libm erf.
@@ -34,7 +36,7 @@
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
 enum { OR_ACT_NONE = 0, OR_ACT_GELU = 1 };
-enum { OR_OK = 0, OR_BAD_ARG = -1, OR_INDEX_DISAGREE = -2, OR_NO_MEMORY = -3 };
+enum { OR_OK = 0, OR_BAD_ARG = -1, OR_NO_MEMORY = -3 };
 
 /* Widen one stored element to double (bf16 is the top half of an IEEE fp32). */
 static double in_at(const void *p, int dtype, int64_t i) {
@@ -51,9 +53,11 @@ double oracle_gelu(double x) { return 0.5 * x * (1.0 + erf(x / sqrt(2.0))); }
 
 static double act_apply(int act, double x) { return act == OR_ACT_GELU ? oracle_gelu(x) : x; }
 
-/* Request of candidate c from the map m and/or the per-request offsets.
- * Returns the request index, -1 if it is not a valid request, -2 if m and offsets disagree. */
-int64_t oracle_request_of(const int32_t *m, const int32_t *off, int64_t R, int64_t c) {
+/* Request of candidate c from the map m and/or the per-request offsets. The offsets, when given,
+ * decide (the candidates of a request are stored contiguously, Sec. 4.2.1); m, when also given,
+ * must agree with them, and *disagree (may be NULL) is set to 1 when it does not.
+ * Returns the request index, or -1 when the candidate has no valid request. */
+int64_t oracle_request_of(const int32_t *m, const int32_t *off, int64_t R, int64_t c, int *disagree) {
     int64_t from_m = -1, from_off = -1;
     if (m) {
         from_m = m[c];
@@ -63,8 +67,8 @@ int64_t oracle_request_of(const int32_t *m, const int32_t *off, int64_t R, int64
         for (int64_t r = 0; r < R; ++r)
             if (off[r] <= c && c < off[r + 1]) { from_off = r; break; }
     }
-    if (m && off && from_m != from_off) return -2;
-    return m ? from_m : from_off;
+    if (disagree) *disagree = m && off && from_m != from_off;
+    return off ? from_off : from_m;
 }
 
 /* ------------------------------------------------------------------------------------------ */
@@ -132,7 +136,6 @@ typedef struct {
     const int64_t *cands;
     double *out;
     int64_t *viol;      /* per-item violation flag */
-    int *disagree;      /* per-item disagreement flag */
 } dca_ctx;
 
 static void dca_item(void *vctx, int64_t i, void *scratch) {
@@ -142,11 +145,11 @@ static void dca_item(void *vctx, int64_t i, void *scratch) {
     double *o = x->out + i * (int64_t)Lq * H * d;
     memset(o, 0, sizeof(double) * (size_t)Lq * H * d);
     x->viol[i] = 0;
-    x->disagree[i] = 0;
     if (c < 0 || c >= x->C) { x->viol[i] = 1; return; }
-    int64_t r = oracle_request_of(x->m, x->off, x->R, c);
-    if (r == -2) { x->disagree[i] = 1; return; }
-    if (r < 0) { x->viol[i] = 1; return; }
+    int disagree = 0;
+    int64_t r = oracle_request_of(x->m, x->off, x->R, c, &disagree);
+    if (r < 0 || disagree) x->viol[i] = 1;
+    if (r < 0) return;
     int64_t base = x->kv_cu ? x->kv_cu[r] : r * (int64_t)x->L;
     int64_t Lr = x->kv_cu ? (int64_t)x->kv_cu[r + 1] - x->kv_cu[r] : x->L;
     if (Lr <= 0) return;
@@ -191,7 +194,8 @@ static void dca_item(void *vctx, int64_t i, void *scratch) {
  * kv_cu: [R+1] prefix offsets of variable K/V lengths, or NULL for uniform length L.
  * L: the uniform length, or the largest L_r when kv_cu is given (sizes the expansion buffer).
  * dtype: storage of k and v; qdtype: storage of q (fp64 lets a chained oracle stay in fp64).
- * Returns OR_OK, or a negative code; *violations counts rows with an invalid request. */
+ * Returns OR_OK, or a negative code; *violations counts candidates with no valid request or with a
+ * map entry that disagrees with the offsets. */
 int oracle_dca(const void *q, int64_t C, int Lq, const void *k, const void *v, int64_t R,
                const int32_t *kv_cu, int L, const int32_t *m, const int32_t *off, int H, int d,
                double scale, int dtype, int qdtype, const int64_t *cands, int64_t n, double *out,
@@ -204,20 +208,15 @@ int oracle_dca(const void *q, int64_t C, int Lq, const void *k, const void *v, i
     if (kv_cu)
         for (int64_t r = 0; r < R; ++r)
             if (kv_cu[r + 1] - kv_cu[r] > L) return OR_BAD_ARG;
-    dca_ctx x = {q, k, v, dtype, qdtype, C, R, Lq, H, d, L, kv_cu, m, off, scale, cands, out, 0, 0};
+    dca_ctx x = {q, k, v, dtype, qdtype, C, R, Lq, H, d, L, kv_cu, m, off, scale, cands, out, 0};
     x.viol = (int64_t *)calloc((size_t)(n > 0 ? n : 1), sizeof(int64_t));
-    x.disagree = (int *)calloc((size_t)(n > 0 ? n : 1), sizeof(int));
-    if (!x.viol || !x.disagree) { free(x.viol); free(x.disagree); return OR_NO_MEMORY; }
+    if (!x.viol) return OR_NO_MEMORY;
     size_t scratch = sizeof(double) * ((size_t)2 * (L > 0 ? L : 1) * H * d + (L > 0 ? L : 1));
     int rc = parallel_for(n, nthreads, scratch, dca_item, &x);
     int64_t nv = 0;
-    for (int64_t i = 0; i < n; ++i) {
-        nv += x.viol[i];
-        if (x.disagree[i]) rc = OR_INDEX_DISAGREE;
-    }
+    for (int64_t i = 0; i < n; ++i) nv += x.viol[i];
     if (violations) *violations = nv;
     free(x.viol);
-    free(x.disagree);
     return rc;
 }
 
@@ -285,7 +284,6 @@ typedef struct {
     const int64_t *cands;
     double *y_c, *y_r_c;       /* [n, N_c last], [n, N_r last] (optional) */
     int64_t *viol;
-    int *disagree;
 } glm_ctx;
 
 static void glm_item(void *vctx, int64_t i, void *scratch) {
@@ -298,11 +296,11 @@ static void glm_item(void *vctx, int64_t i, void *scratch) {
     memset(yc, 0, sizeof(double) * (size_t)nc_last);
     if (yrc) memset(yrc, 0, sizeof(double) * (size_t)nr_last);
     x->viol[i] = 0;
-    x->disagree[i] = 0;
     if (c < 0 || c >= x->C) { x->viol[i] = 1; return; }
-    int64_t r = oracle_request_of(x->m, x->off, x->R, c);
-    if (r == -2) { x->disagree[i] = 1; return; }
-    if (r < 0) { x->viol[i] = 1; return; }
+    int disagree = 0;
+    int64_t r = oracle_request_of(x->m, x->off, x->R, c, &disagree);
+    if (r < 0 || disagree) x->viol[i] = 1;
+    if (r < 0) return;
     double *u = (double *)scratch, *y = u + x->width_max;
     /* The explicit broadcast: u_c = [x_r[m(c)]; x_c[c]]. */
     for (int j = 0; j < x->k_req0; ++j) u[j] = in_at(x->x_r, x->dtype, r * x->k_req0 + j);
@@ -363,10 +361,9 @@ int oracle_glm(const void *x_r, int64_t R, const void *x_c, int64_t C, const int
     for (int l = 0; l < nlayers && rc == OR_OK; ++l) rc = build_dense(&layers[l], dtype, &D[l]);
     if (!cands) n = C;
     glm_ctx x = {x_r, x_c, dtype, R, C, m, off, nlayers, D, layers[0].k_req, layers[0].k_cand, width_max,
-                 cands, y_c, y_r_c, 0, 0};
+                 cands, y_c, y_r_c, 0};
     x.viol = (int64_t *)calloc((size_t)(n > 0 ? n : 1), sizeof(int64_t));
-    x.disagree = (int *)calloc((size_t)(n > 0 ? n : 1), sizeof(int));
-    if (!x.viol || !x.disagree) rc = OR_NO_MEMORY;
+    if (!x.viol) rc = OR_NO_MEMORY;
     if (rc == OR_OK) rc = parallel_for(n, nthreads, sizeof(double) * 2 * (size_t)width_max, glm_item, &x);
     if (rc == OR_OK && y_r) {
         double *buf = (double *)malloc(sizeof(double) * 2 * (size_t)width_max);
@@ -376,24 +373,23 @@ int oracle_glm(const void *x_r, int64_t R, const void *x_c, int64_t C, const int
     }
     int64_t nv = 0;
     if (x.viol)
-        for (int64_t i = 0; i < n; ++i) {
-            nv += x.viol[i];
-            if (x.disagree[i] && rc == OR_OK) rc = OR_INDEX_DISAGREE;
-        }
+        for (int64_t i = 0; i < n; ++i) nv += x.viol[i];
     if (violations) *violations = nv;
     for (int l = 0; l < nlayers; ++l) { free(D[l].w); free(D[l].b); }
     free(D);
     free(x.viol);
-    free(x.disagree);
     return rc;
 }
 
-/* Index checks: counts candidates whose m is outside [0, R), offsets that are not a monotone
- * partition of [0, C), and candidates whose m disagrees with the offsets. */
+/* Index checks, one count per fault: with offsets, off[0] != 0 and off[R] != C count once each
+ * and every decreasing step off[r + 1] < off[r] once; with a map, every candidate whose m is
+ * outside [0, R), and with sorted_flag every candidate whose m is below its predecessor's; with
+ * both, every candidate with a valid m that does not lie in [off[m], off[m + 1]). */
 int64_t oracle_index_violations(const int32_t *m, const int32_t *off, int64_t C, int64_t R, int sorted_flag) {
     int64_t bad = 0;
     if (off) {
-        if (off[0] != 0 || off[R] != C) ++bad;
+        if (off[0] != 0) ++bad;
+        if (off[R] != C) ++bad;
         for (int64_t r = 0; r < R; ++r)
             if (off[r + 1] < off[r]) ++bad;
     }

@@ -189,10 +189,20 @@ def test_offsets_and_map_agree():
     b = oracle.dca(q, k4, v4, s.R, off=s.offsets)
     c = oracle.dca(q, k4, v4, s.R, m=s.cand_to_req, off=s.offsets)
     assert np.array_equal(a, b) and np.array_equal(a, c)
+    # A map that disagrees with the offsets: the offsets decide every row (the contiguous grouping
+    # the kernels execute on) and the disagreeing entry is counted as one violation.
     bad = s.cand_to_req.copy()
     bad[3] = (bad[3] + 1) % s.R
-    with pytest.raises(oracle.OracleError):
-        oracle.dca(q, k4, v4, s.R, m=bad, off=s.offsets)
+    got, nv = oracle.dca(q, k4, v4, s.R, m=bad, off=s.offsets, return_violations=True)
+    assert nv == 1 and np.array_equal(got, b)
+    assert oracle.index_violations(bad, s.offsets, len(bad), s.R) == 1
+    # ... and an out-of-range entry inside a valid offset range likewise
+    bad[5] = -7
+    got, nv = oracle.dca(q, k4, v4, s.R, m=bad, off=s.offsets, return_violations=True)
+    assert nv == 2 and np.array_equal(got, b)
+    # the map alone for the same entries: row 3 attends another request, row 5 is zero
+    alone, nv = oracle.dca(q, k4, v4, s.R, m=bad, return_violations=True)
+    assert nv == 1 and np.all(alone[5] == 0) and not np.array_equal(alone[3], b[3])
 
 
 def test_invalid_request_rows_are_zero_and_counted():

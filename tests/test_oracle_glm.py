@@ -207,3 +207,27 @@ def test_index_violation_counter():
     assert oracle.index_violations(np.array([0, 0, 1, 3, 2], np.int32), None, 5, 3, False) == 1
     assert oracle.index_violations(None, np.array([0, 3, 2, 5], np.int32), 5, 3, False) == 1
     assert oracle.index_violations(m, np.array([0, 1, 4, 5], np.int32), 5, 3, False) == 1
+    # the ends of the offsets count once each
+    assert oracle.index_violations(None, np.array([1, 2, 4, 5], np.int32), 5, 3, False) == 1
+    assert oracle.index_violations(None, np.array([0, 2, 4, 4], np.int32), 5, 3, False) == 1
+    assert oracle.index_violations(None, np.array([1, 2, 4, 6], np.int32), 5, 3, False) == 2
+    # an unsorted map is a violation only when the caller declares it sorted
+    u = np.array([2, 0, 1, 0, 1], np.int32)
+    assert oracle.index_violations(u, None, 5, 3, False) == 0
+    assert oracle.index_violations(u, None, 5, 3, True) == 2
+
+
+def test_map_that_disagrees_with_offsets_takes_the_offsets():
+    # Both index forms given and disagreeing: each candidate's request comes from the offsets (the
+    # contiguous grouping) and every disagreeing entry is one violation.
+    x_r = _f32(7, 1, (3, 8))
+    x_c = _f32(7, 2, (5, 8))
+    ly = _layer(7, 8, 8, 4, 4, "gelu")
+    off = np.array([0, 2, 4, 5], np.int32)
+    bad = np.array([0, 2, 1, 1, -1], np.int32)
+    ref = oracle.glm(x_r, x_c, [ly], off=off)
+    out = oracle.glm(x_r, x_c, [ly], m=bad, off=off, return_violations=True)
+    assert out["violations"] == 2
+    assert np.array_equal(out["y_c"], ref["y_c"])
+    assert oracle.request_of(bad, off, 3, 1) == 0 and oracle.request_of(bad, None, 3, 1) == 2
+    assert oracle.index_violations(bad, off, 5, 3, False) == 2
