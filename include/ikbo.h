@@ -18,12 +18,15 @@
  *  - Errors: a status code is returned, never an exception. The last failure's text is kept per
  *    host thread (ikbo_last_error_message). Argument checks run before any GPU work, so a call
  *    that returns an error other than IKBO_HIP_ERROR has enqueued nothing.
- *  - Index arrays: cand_to_req (the map m, int32 [num_cand]) and/or req_cand_offsets (int32
- *    [num_req + 1], candidates of request r are rows off[r]..off[r+1]-1). At least one is
- *    required. The pages store the candidates of one request contiguously (Sec. 4.2.1); a map
- *    that is not grouped is accepted too. Index CONTENTS are a precondition that
- *    ikbo_check_index verifies; kernels stay memory-safe whatever the contents: a candidate
- *    whose request is out of range gets an all-zero output row.
+ *  - Index arrays: cand_to_req (the map m of Sec. 4.1, int32 [num_cand]) and/or
+ *    req_cand_offsets (int32 [num_req + 1], candidates of request r are rows off[r]..off[r+1]-1).
+ *    At least one is required. The pages store the candidates of one request contiguously
+ *    (Sec. 4.2.1); a map that is not grouped is accepted too (grouped on the device by a stable
+ *    sort: a request's candidates keep their index order). When both are given they must agree,
+ *    and in every entry point the offsets then decide each candidate's request: cand_to_req is
+ *    not read. Index CONTENTS (range, order, agreement) are a precondition that ikbo_check_index
+ *    verifies; kernels stay memory-safe whatever the contents: a candidate with no request in
+ *    range (or outside every offset range) gets an all-zero output row.
  *  - Dtypes: inputs IKBO_F32 or IKBO_BF16; outputs IKBO_F32 or IKBO_BF16; accumulation is
  *    always fp32. A bf16-output call returns the round-to-nearest-even bf16 of what the same
  *    call with an fp32 output returns.
@@ -84,8 +87,8 @@ const char *ikbo_last_error_message(void);
  *       kv_cu_seqlens[r] .. kv_cu_seqlens[r+1]-1                       (in_dtype)
  * kv_cu_seqlens  device int32 [num_req + 1] or NULL (uniform length kv_len)
  * kv_len         uniform K/V length, or with kv_cu_seqlens an upper bound on L_r (0 = unknown)
- * cand_to_req, req_cand_offsets, index_flags   see the conventions above; when offsets are
- *       given they define the grouping and cand_to_req is not read.
+ * cand_to_req, req_cand_offsets, index_flags   see the conventions above (the offsets, when
+ *       given, define the grouping).
  * num_heads      H >= 1 (queries and keys share the head count)
  * head_dim       bf16: 64 or 128; fp32: a multiple of 4 in [4, 128]
  *       bf16 also needs each request's K (and V) rows to span fewer than 2^31 bytes,
@@ -124,14 +127,17 @@ int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len,
  * activation  IKBO_ACT_NONE or IKBO_ACT_GELU, applied to both groups
  * y_req  [num_req, n_req_out] (out_dtype) or NULL to skip the request-group output
  * y_cand [num_cand, n_cand_out] (out_dtype)
- * k_req, k_cand, n_req_out, n_cand_out: >= 0; with bf16 the K widths must be multiples of 8 and
- *       with fp32 multiples of 4 (16-byte rows), else IKBO_MISALIGNED -- the zero padding of
- *       Sec. 4.2.4 is the caller's transform.
- * workspace >= ikbo_lcb_workspace_size(num_cand, num_req, k_req, n_req_out, n_cand_out) bytes;
- *       it holds Z in fp32 and the request GEMM's split-K partial sums.
+ * k_req, k_cand, n_req_out, n_cand_out: >= 0, any value. The alignment rule of Sec. 4.2.4 is
+ *       applied inside the call: a bf16 K width that is not a multiple of 8 (16-byte rows) is
+ *       zero-padded to the next multiple of 8 in workspace copies of the activations and of the
+ *       weights that multiply them (the padded columns add nothing to any sum); fp32 widths need
+ *       no padding. Base pointers must still be 16-byte aligned.
+ * workspace >= ikbo_lcb_workspace_size(num_cand, num_req, k_req, k_cand, n_req_out, n_cand_out,
+ *       in_dtype) bytes; it holds the candidate->request map built from the offsets, Z in fp32,
+ *       the request GEMM's split-K partial sums and, for misaligned bf16 K widths, the padded copies.
  * ---------------------------------------------------------------------------------------- */
-size_t ikbo_lcb_workspace_size(int64_t num_cand, int64_t num_req, int32_t k_req,
-                               int32_t n_req_out, int32_t n_cand_out);
+size_t ikbo_lcb_workspace_size(int64_t num_cand, int64_t num_req, int32_t k_req, int32_t k_cand,
+                               int32_t n_req_out, int32_t n_cand_out, int32_t in_dtype);
 
 int ikbo_lcb_forward(const void *x_req, int64_t num_req, int32_t k_req,
                      const void *x_cand, int64_t num_cand, int32_t k_cand,
@@ -147,7 +153,8 @@ int ikbo_lcb_forward(const void *x_req, int64_t num_req, int32_t k_req,
  * (Sec. 3.1.5, Eq. 11), as used to form DCA queries (Sec. 3.2, Eq. 12). Layer l+1 takes
  * layer l's outputs: k_req(l+1) = n_req_out(l), k_cand(l+1) = n_cand_out(l). Hidden
  * activations live in the workspace, in bf16 for bf16 inputs and fp32 for fp32 inputs; the
- * last layer writes y_req / y_cand in out_dtype.
+ * last layer writes y_req / y_cand in out_dtype. Widths may take any value (each layer applies
+ * the zero padding rule of ikbo_lcb_forward to its own inputs).
  * `layers` is a HOST array of num_layers descriptors whose pointer members are device
  * pointers.
  * ---------------------------------------------------------------------------------------- */
@@ -308,12 +315,17 @@ int ikbo_lcb_emb_forward(const void *x_req, int64_t num_req, int32_t n_req_in,
                          size_t workspace_bytes, void *hip_stream);
 
 /* ------------------------------------------------------------------------------------------
- * Index check: counts, on the device, (a) candidates whose cand_to_req is outside
- * [0, num_req), (b) with IKBO_INDEX_SORTED, candidates whose map value is below the previous
- * candidate's, (c) when both arrays are given, candidates that are not inside
- * [off[m(c)], off[m(c)+1]), and (d) offsets that are not a non-decreasing partition of
- * [0, num_cand) (each bad offset entry counts once, off[0] != 0 and off[R] != C once each).
- * d_violations: device uint64 [1], overwritten with the count (0 = valid).
+ * Index check (the map m of Sec. 4.1, the contiguous grouping of Sec. 4.2.1): counts, on the
+ * device, one violation per fault:
+ *   (a) each candidate whose cand_to_req is outside [0, num_req);
+ *   (b) with IKBO_INDEX_SORTED, each candidate whose map value is below the previous candidate's;
+ *   (c) when both arrays are given, each candidate with a valid map value that does not lie in
+ *       [off[m(c)], off[m(c)+1]) (the two forms disagree);
+ *   (d) with offsets, off[0] != 0 and off[num_req] != num_cand (one each) and every decreasing
+ *       step off[r+1] < off[r].
+ * Either index array may be NULL (not both when num_cand > 0). d_violations: device uint64 [1],
+ * 8-byte aligned, overwritten with the count (0 = valid) in stream order; the caller reads it
+ * after the stream synchronises. Errors: IKBO_INVALID_ARGUMENT, IKBO_MISALIGNED, IKBO_HIP_ERROR.
  * ---------------------------------------------------------------------------------------- */
 int ikbo_check_index(const int32_t *cand_to_req, const int32_t *req_cand_offsets,
                      int64_t num_cand, int64_t num_req, uint32_t index_flags,

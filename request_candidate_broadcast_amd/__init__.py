@@ -112,7 +112,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ikbo_dca_forward.argtypes = [vp, i64, i32, vp, vp, i64, vp, i32, vp, vp, u32, i32, i32, f32, i32, i32, vp,
                                      vp, sz, vp]
     lib.ikbo_lcb_workspace_size.restype = sz
-    lib.ikbo_lcb_workspace_size.argtypes = [i64, i64, i32, i32, i32]
+    lib.ikbo_lcb_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32, i32]
     lib.ikbo_lcb_forward.restype = ctypes.c_int
     lib.ikbo_lcb_forward.argtypes = [vp, i64, i32, vp, i64, i32, vp, vp, u32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                      i32, vp, vp, vp, sz, vp]
@@ -393,8 +393,10 @@ def ikbo_kv_project(s: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, *, ou
 
 
 # ------------------------------------------------------------------------------------------------
-def ikbo_lcb_workspace_size(num_cand: int, num_req: int, k_req: int, n_req_out: int, n_cand_out: int) -> int:
-    return int(load_library().ikbo_lcb_workspace_size(num_cand, num_req, k_req, n_req_out, n_cand_out))
+def ikbo_lcb_workspace_size(num_cand: int, num_req: int, k_req: int, k_cand: int, n_req_out: int, n_cand_out: int,
+                            dtype=torch.bfloat16) -> int:
+    code = _dt(torch.empty(0, dtype=dtype))
+    return int(load_library().ikbo_lcb_workspace_size(num_cand, num_req, k_req, k_cand, n_req_out, n_cand_out, code))
 
 
 def ikbo_lcb_forward(x_req: torch.Tensor, x_cand: torch.Tensor, w_rr: torch.Tensor, w_cr: torch.Tensor,
@@ -425,7 +427,7 @@ def ikbo_lcb_forward(x_req: torch.Tensor, x_cand: torch.Tensor, w_rr: torch.Tens
         y_cand = torch.empty((C, N_c), dtype=_torch_dtype(out_code), device=dev)
     if want_request_output and y_req is None:
         y_req = torch.empty((R, N_r), dtype=_torch_dtype(out_code), device=dev)
-    ws = _workspace(ikbo_lcb_workspace_size(C, R, K_r, N_r, N_c), dev, workspace)
+    ws = _workspace(ikbo_lcb_workspace_size(C, R, K_r, K_c, N_r, N_c, x_req.dtype), dev, workspace)
     st = lib.ikbo_lcb_forward(_ptr(x_req), R, K_r, _ptr(x_cand), C, K_c, _ptr(cand_to_req), _ptr(req_cand_offsets),
                               IKBO_INDEX_SORTED if sorted_index else 0, _ptr(w_rr), _ptr(w_cr), _ptr(w_cc),
                               _ptr(b_r), _ptr(b_c), N_r, N_c, ACTIVATIONS[activation], in_code, out_code,

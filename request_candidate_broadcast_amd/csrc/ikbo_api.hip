@@ -62,17 +62,22 @@ struct Carver {
 };
 
 // ---- DCA ----------------------------------------------------------------------------------------
-size_t dca_ws(int64_t C, int64_t R, Carver *c, int32_t **counts, int32_t **off, int32_t **tiles, int32_t **perm) {
+// counts [R+1], off [R+1], tiles [R+1], perm [C], then the stable grouping's scratch (used only
+// when the map is given without offsets)
+size_t dca_ws(int64_t C, int64_t R, Carver *c, int32_t **counts, int32_t **off, int32_t **tiles, int32_t **perm,
+              int32_t **sort_scratch = nullptr) {
     Carver local(nullptr);
     Carver &cv = c ? *c : local;
     int32_t *a = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(R + 1));
     int32_t *b = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(R + 1));
     int32_t *t = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(R + 1));
     int32_t *p = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
+    int32_t *g = (int32_t *)cv.take(sizeof(int32_t) * (size_t)ikbo::stable_group_scratch_ints(C > 0 ? C : 1));
     if (counts) *counts = a;
     if (off) *off = b;
     if (tiles) *tiles = t;
     if (perm) *perm = p;
+    if (sort_scratch) *sort_scratch = g;
     return cv.used;
 }
 
@@ -87,6 +92,41 @@ bool getenv_flag(const char *name) {
     return v && v[0] == '1';
 }
 
+// Alignment rule (Sec. 4.2.4): a bf16 K width that is not a multiple of 8 elements (16-byte rows)
+// is zero-padded to the next multiple of 8, in copies of the activations and of the weights that
+// multiply them, so the GEMMs run on whole 16-byte rows; the padded columns multiply zeros and
+// change no sum. Bytes of each padded copy one LCB layer needs (0 when its width is aligned).
+int64_t round_up8(int64_t k) { return (k + 7) / 8 * 8; }
+
+struct PadSizes {
+    size_t xr = 0, wrr = 0, wcr = 0, xc = 0, wcc = 0;
+    void take_max(const PadSizes &o) {
+        xr = xr > o.xr ? xr : o.xr;
+        wrr = wrr > o.wrr ? wrr : o.wrr;
+        wcr = wcr > o.wcr ? wcr : o.wcr;
+        xc = xc > o.xc ? xc : o.xc;
+        wcc = wcc > o.wcc ? wcc : o.wcc;
+    }
+};
+
+PadSizes lcb_pad_sizes(int64_t C, int64_t R, int32_t k_req, int32_t k_cand, int32_t n_req, int32_t n_cand,
+                       int32_t in_dtype) {
+    PadSizes p;
+    if (in_dtype != IKBO_BF16) return p;      // the fp32 kernel reads elements one by one
+    if (k_req % 8) {
+        const size_t kp = (size_t)round_up8(k_req) * 2;
+        p.xr = kp * (size_t)R;
+        p.wrr = kp * (size_t)n_req;
+        p.wcr = kp * (size_t)n_cand;
+    }
+    if (k_cand % 8) {
+        const size_t kp = (size_t)round_up8(k_cand) * 2;
+        p.xc = kp * (size_t)C;
+        p.wcc = kp * (size_t)n_cand;
+    }
+    return p;
+}
+
 struct LcbWs {
     int32_t *map = nullptr;
     float *z = nullptr;
@@ -94,26 +134,33 @@ struct LcbWs {
     size_t partial_cap = 0;   // floats
     int32_t *sync = nullptr;  // state of the persistent LCB launch
     int64_t sync_cap = 0;     // int32 words
+    // zero-padded copies for misaligned K widths (see lcb_pad_sizes), each at least its size
+    void *pad_xr = nullptr, *pad_wrr = nullptr, *pad_wcr = nullptr, *pad_xc = nullptr, *pad_wcc = nullptr;
 };
 
-size_t lcb_ws(int64_t C, int64_t R, int32_t k_req, int32_t n_req, int32_t n_cand, int32_t in_dtype, Carver *c,
-              LcbWs *w, bool with_map = true) {
+void carve_pads(Carver &cv, const PadSizes &p, LcbWs *w) {
+    void *a = cv.take(p.xr), *b = cv.take(p.wrr), *c = cv.take(p.wcr), *d = cv.take(p.xc), *e = cv.take(p.wcc);
+    if (w) {
+        w->pad_xr = a;
+        w->pad_wrr = b;
+        w->pad_wcr = c;
+        w->pad_xc = d;
+        w->pad_wcc = e;
+    }
+}
+
+size_t lcb_ws(int64_t C, int64_t R, int32_t k_req, int32_t k_cand, int32_t n_req, int32_t n_cand, int32_t in_dtype,
+              Carver *c, LcbWs *w) {
     Carver local(nullptr);
     Carver &cv = c ? *c : local;
     const int32_t n_total = n_req + n_cand;
-    int32_t s = 1;
-    if (in_dtype < 0) {  // size for either dtype
-        s = lcb_splits(R, n_total, k_req, IKBO_F32);
-        int32_t s2 = lcb_splits(R, n_total, k_req, IKBO_BF16);
-        if (s2 > s) s = s2;
-    } else {
-        s = lcb_splits(R, n_total, k_req, in_dtype);
-    }
-    int32_t *map = with_map ? (int32_t *)cv.take(sizeof(int32_t) * (size_t)(C > 0 ? C : 1)) : nullptr;
+    const int32_t s = lcb_splits(R, n_total, k_req, in_dtype);
+    int32_t *map = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
     float *z = (float *)cv.take(sizeof(float) * (size_t)(R > 0 ? R : 1) * (size_t)(n_cand > 0 ? n_cand : 1));
     float *part = (float *)cv.take(sizeof(float) * (size_t)s * (size_t)(R > 0 ? R : 1) * (size_t)(n_total > 0 ? n_total : 1));
     const int64_t nsync = ikbo::lcb_fused_sync_ints(R > 0 ? R : 1, n_total > 0 ? n_total : 1);
     int32_t *sync = (int32_t *)cv.take(sizeof(int32_t) * (size_t)nsync);
+    carve_pads(cv, lcb_pad_sizes(C, R, k_req, k_cand, n_req, n_cand, in_dtype), w);
     if (w) {
         w->map = map;
         w->z = z;
@@ -132,6 +179,33 @@ int run_lcb(const void *x_req, int64_t R, int32_t k_req, const void *x_cand, int
             void *y_req, void *y_cand, int64_t ldo_r, int64_t ldo_c, const LcbWs &ws, hipStream_t s) {
     const int in_f32 = in_dtype == IKBO_F32;
     const bool want_req = y_req != nullptr && n_req > 0;
+    // alignment rule: bf16 K widths off a multiple of 8 run on zero-padded copies
+    if (!in_f32 && k_req % 8) {
+        const int32_t kp = (int32_t)round_up8(k_req);
+        if (R > 0) {
+            IKBO_HIP(ikbo::launch_pad_rows_bf16(x_req, R, k_req, ws.pad_xr, kp, s));
+            x_req = ws.pad_xr;
+        }
+        if (want_req) {
+            IKBO_HIP(ikbo::launch_pad_rows_bf16(w_rr, n_req, k_req, ws.pad_wrr, kp, s));
+            w_rr = ws.pad_wrr;
+        }
+        if (n_cand > 0) {
+            IKBO_HIP(ikbo::launch_pad_rows_bf16(w_cr, n_cand, k_req, ws.pad_wcr, kp, s));
+            w_cr = ws.pad_wcr;
+        }
+        k_req = kp;
+    }
+    if (!in_f32 && k_cand % 8 && n_cand > 0) {
+        const int32_t kp = (int32_t)round_up8(k_cand);
+        if (C > 0) {
+            IKBO_HIP(ikbo::launch_pad_rows_bf16(x_cand, C, k_cand, ws.pad_xc, kp, s));
+            x_cand = ws.pad_xc;
+        }
+        IKBO_HIP(ikbo::launch_pad_rows_bf16(w_cc, n_cand, k_cand, ws.pad_wcc, kp, s));
+        w_cc = ws.pad_wcc;
+        k_cand = kp;
+    }
     // bf16 with both GEMMs on direct copies, IKBO_LCB_FUSED=1: one persistent launch that
     // co-schedules the request tiles and the candidate tiles (Sec. 4.2.3). Its results equal the
     // two launches below bit for bit; on this part the two launches are faster (the split-K
@@ -246,10 +320,7 @@ int check_layer_dims(int32_t k_req, int32_t k_cand, int32_t n_req, int32_t n_can
         return fail(IKBO_INVALID_ARGUMENT, "negative layer width (k_req %d k_cand %d n_req %d n_cand %d)", k_req, k_cand,
                     n_req, n_cand);
     if (act != IKBO_ACT_NONE && act != IKBO_ACT_GELU) return fail(IKBO_INVALID_ARGUMENT, "unknown activation %d", act);
-    const int vec = in_dtype == IKBO_F32 ? 4 : 8;
-    if (k_req % vec || k_cand % vec)
-        return fail(IKBO_MISALIGNED, "k_req %d / k_cand %d must be multiples of %d (zero-pad the inputs and weights)",
-                    k_req, k_cand, vec);
+    (void)in_dtype;     // any K width: bf16 widths off a multiple of 8 are zero-padded in the workspace
     return IKBO_OK;
 }
 
@@ -334,19 +405,23 @@ static int dca_run(const void *q, int64_t C, int32_t q_len, const void *k, const
     const int mode = in_f32 ? 0 : rows_all <= 32 * R ? 1 : rows_all <= 1024 * R ? 2 : 0;
 
     Carver cv(workspace);
-    int32_t *counts, *off, *tiles, *perm;
-    dca_ws(C, R, &cv, &counts, &off, &tiles, &perm);
+    int32_t *counts, *off, *tiles, *perm, *sort_scratch;
+    dca_ws(C, R, &cv, &counts, &off, &tiles, &perm, &sort_scratch);
     const int32_t bm = ikbo::dca_block_m(head_dim, in_f32, mode);
     const int32_t *perm_used = nullptr;
     if (req_cand_offsets) {
+        // the offsets define the grouping (cand_to_req, if also given, is not read)
         IKBO_HIP(ikbo::launch_scan_tiles(nullptr, req_cand_offsets, R, C, q_len, num_heads, bm, off, nullptr, tiles, s));
         IKBO_HIP(ikbo::launch_zero_uncovered(req_cand_offsets, R, C, out, row_elems, o_cs, ob, s));
     } else {
-        // group an arbitrary map: histogram -> scan -> scatter (the scan leaves the cursor in counts)
+        // group an arbitrary map: counts -> offsets and tiles, then a stable sort of the candidates
+        // by request (each request's candidates keep their index order); rows without a valid
+        // request are zeroed
         IKBO_HIP(ikbo::launch_fill_i32(counts, R + 1, 0, s));
         IKBO_HIP(ikbo::launch_histogram(cand_to_req, C, R, counts, s));
-        IKBO_HIP(ikbo::launch_scan_tiles(counts, nullptr, R, C, q_len, num_heads, bm, off, counts, tiles, s));
-        IKBO_HIP(ikbo::launch_scatter(cand_to_req, C, R, counts, perm, out, row_elems, o_cs, ob, s));
+        IKBO_HIP(ikbo::launch_scan_tiles(counts, nullptr, R, C, q_len, num_heads, bm, off, nullptr, tiles, s));
+        IKBO_HIP(ikbo::launch_stable_group(cand_to_req, C, R, perm, sort_scratch, s));
+        IKBO_HIP(ikbo::launch_zero_invalid_rows(cand_to_req, C, R, out, row_elems, o_cs, ob, s));
         perm_used = perm;
     }
     if (R == 0) return ok();
@@ -395,25 +470,36 @@ size_t ikbo_request_attention_workspace_size(int64_t num_req) {
 }
 
 // q_cs / o_cs: elements between consecutive requests' query (output) rows; 0 means packed.
-static int request_attention_impl(const void *q_req, int64_t num_req, int32_t q_len, const void *k, const void *v,
-                                  const int32_t *kv_cu_seqlens, int32_t kv_len, int32_t num_heads, int32_t head_dim,
-                                  float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out, void *workspace,
-                                  size_t workspace_bytes, void *hip_stream, int64_t q_cs, int64_t o_cs) {
+// Argument checks of the request-side attention (nothing enqueued)
+static int request_attention_check(const void *q_req, int64_t num_req, int32_t q_len, const void *k, const void *v,
+                                   const int32_t *kv_cu_seqlens, int32_t kv_len, int32_t num_heads, int32_t head_dim,
+                                   int32_t in_dtype, int32_t out_dtype, const void *out, void *workspace,
+                                   size_t workspace_bytes) {
     const int64_t R = num_req;
     if (R < 0) return fail(IKBO_INVALID_ARGUMENT, "negative num_req");
     const size_t need = ikbo_request_attention_workspace_size(R);
     if (workspace_bytes < need || !workspace)
         return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
     if (!aligned16(workspace)) return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    Carver cv(workspace);
+    int32_t *ident = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(R + 1));
+    return dca_validate(q_req, R, q_len, k, v, R, kv_cu_seqlens, kv_len, nullptr, ident, IKBO_INDEX_SORTED, num_heads,
+                        head_dim, in_dtype, out_dtype, out, (char *)workspace + cv.used, workspace_bytes - cv.used);
+}
+
+static int request_attention_impl(const void *q_req, int64_t num_req, int32_t q_len, const void *k, const void *v,
+                                  const int32_t *kv_cu_seqlens, int32_t kv_len, int32_t num_heads, int32_t head_dim,
+                                  float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream, int64_t q_cs, int64_t o_cs) {
+    const int64_t R = num_req;
+    const int rc = request_attention_check(q_req, R, q_len, k, v, kv_cu_seqlens, kv_len, num_heads, head_dim, in_dtype,
+                                           out_dtype, out, workspace, workspace_bytes);
+    if (rc) return rc;
+    if (R == 0) return ok();
     // the identity map as offsets (request r is candidate r), then the DCA over it
     Carver cv(workspace);
     int32_t *ident = (int32_t *)cv.take(sizeof(int32_t) * (size_t)(R + 1));
     void *rest = (char *)workspace + cv.used;
-    const size_t rest_bytes = workspace_bytes - cv.used;
-    const int rc = dca_validate(q_req, R, q_len, k, v, R, kv_cu_seqlens, kv_len, nullptr, ident, IKBO_INDEX_SORTED,
-                                num_heads, head_dim, in_dtype, out_dtype, out, rest, rest_bytes);
-    if (rc) return rc;
-    if (R == 0) return ok();
     hipStream_t s = (hipStream_t)hip_stream;
     IKBO_HIP(ikbo::launch_iota_i32(ident, R + 1, s));
     return dca_run(q_req, R, q_len, k, v, R, kv_cu_seqlens, kv_len, nullptr, ident, num_heads, head_dim, softmax_scale,
@@ -539,18 +625,27 @@ int ikbo_lcb_emb_forward(const void *x_req, int64_t num_req, int32_t n_req_in, c
 }
 
 // ---- K/V projection -----------------------------------------------------------------------------
-int ikbo_kv_project(const void *s_rows, int64_t rows, int32_t d_in, const void *w_k, const void *w_v, int32_t d_out,
-                    int32_t in_dtype, int32_t out_dtype, void *k_out, void *v_out, void *hip_stream) {
+// Argument checks of the K/V projection (nothing enqueued)
+static int kv_project_check(const void *s_rows, int64_t rows, int32_t d_in, const void *w_k, const void *w_v,
+                            int32_t d_out, int32_t in_dtype, int32_t out_dtype, const void *k_out, const void *v_out) {
     if (rows < 0 || d_in < 0 || d_out < 0)
         return fail(IKBO_INVALID_ARGUMENT, "bad sizes (rows %lld d_in %d d_out %d)", (long long)rows, d_in, d_out);
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(IKBO_UNSUPPORTED, "dtype in %d out %d", in_dtype, out_dtype);
-    if (rows == 0 || d_out == 0) return ok();
+    if (rows == 0 || d_out == 0) return IKBO_OK;
     if (!s_rows || !w_k || !w_v || !k_out || !v_out) return fail(IKBO_INVALID_ARGUMENT, "a tensor pointer is NULL");
     const void *ptrs[] = {s_rows, w_k, w_v, k_out, v_out};
     for (const void *p : ptrs)
         if (!aligned16(p)) return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
+    if (d_in % (in_dtype == IKBO_F32 ? 4 : 8)) return fail(IKBO_MISALIGNED, "d_in must keep 16-byte rows (got %d)", d_in);
+    return IKBO_OK;
+}
+
+int ikbo_kv_project(const void *s_rows, int64_t rows, int32_t d_in, const void *w_k, const void *w_v, int32_t d_out,
+                    int32_t in_dtype, int32_t out_dtype, void *k_out, void *v_out, void *hip_stream) {
+    const int rc = kv_project_check(s_rows, rows, d_in, w_k, w_v, d_out, in_dtype, out_dtype, k_out, v_out);
+    if (rc) return rc;
+    if (rows == 0 || d_out == 0) return ok();
     const int in_f32 = in_dtype == IKBO_F32;
-    if (d_in % (in_f32 ? 4 : 8)) return fail(IKBO_MISALIGNED, "d_in must keep 16-byte rows (got %d)", d_in);
     hipStream_t s = (hipStream_t)hip_stream;
     // one GEMM per projection: out = s W^T, no bias, no activation, no gather
     for (int which = 0; which < 2; ++which) {
@@ -572,10 +667,11 @@ int ikbo_kv_project(const void *s_rows, int64_t rows, int32_t d_in, const void *
     return ok();
 }
 
-size_t ikbo_lcb_workspace_size(int64_t num_cand, int64_t num_req, int32_t k_req, int32_t n_req_out,
-                               int32_t n_cand_out) {
-    if (num_cand < 0 || num_req < 0 || k_req < 0 || n_req_out < 0 || n_cand_out < 0) return 0;
-    return lcb_ws(num_cand, num_req, k_req, n_req_out, n_cand_out, -1, nullptr, nullptr);
+size_t ikbo_lcb_workspace_size(int64_t num_cand, int64_t num_req, int32_t k_req, int32_t k_cand, int32_t n_req_out,
+                               int32_t n_cand_out, int32_t in_dtype) {
+    if (num_cand < 0 || num_req < 0 || k_req < 0 || k_cand < 0 || n_req_out < 0 || n_cand_out < 0 || !dtype_ok(in_dtype))
+        return 0;
+    return lcb_ws(num_cand, num_req, k_req, k_cand, n_req_out, n_cand_out, in_dtype, nullptr, nullptr);
 }
 
 int ikbo_lcb_forward(const void *x_req, int64_t num_req, int32_t k_req, const void *x_cand, int64_t num_cand,
@@ -599,20 +695,29 @@ int ikbo_lcb_forward(const void *x_req, int64_t num_req, int32_t k_req, const vo
     const void *ptrs[] = {x_req, x_cand, w_rr, w_cr, w_cc, b_r, b_c, y_req, y_cand, workspace};
     for (const void *p : ptrs)
         if (!aligned16(p)) return fail(IKBO_MISALIGNED, "tensor base pointers must be 16-byte aligned");
-    const size_t need = ikbo_lcb_workspace_size(C, R, k_req, n_req_out, n_cand_out);
+    const size_t need = ikbo_lcb_workspace_size(C, R, k_req, k_cand, n_req_out, n_cand_out, in_dtype);
     if (workspace_bytes < need || !workspace) return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
     hipStream_t s = (hipStream_t)hip_stream;
     Carver cv(workspace);
     LcbWs ws;
-    lcb_ws(C, R, k_req, n_req_out, n_cand_out, -1, &cv, &ws);
+    lcb_ws(C, R, k_req, k_cand, n_req_out, n_cand_out, in_dtype, &cv, &ws);
+    // the offsets, when given, define each candidate's request (as in every entry point)
     const int32_t *map = cand_to_req;
-    if (!map) {
+    if (req_cand_offsets) {
         IKBO_HIP(ikbo::launch_offsets_to_map(req_cand_offsets, R, C, ws.map, s));
         map = ws.map;
     }
     rc = run_lcb(x_req, R, k_req, x_cand, C, k_cand, map, w_rr, w_cr, w_cc, b_r, b_c, n_req_out, n_cand_out, activation,
                  in_dtype, out_dtype, y_req, y_cand, n_req_out, n_cand_out, ws, s);
     return rc ? rc : ok();
+}
+
+static PadSizes glm_pad_sizes(int64_t C, int64_t R, int32_t num_layers, const ikbo_glm_layer *layers, int32_t in_dtype) {
+    PadSizes p;
+    for (int l = 0; l < num_layers; ++l)
+        p.take_max(lcb_pad_sizes(C, R, layers[l].k_req, layers[l].k_cand, layers[l].n_req_out, layers[l].n_cand_out,
+                                 in_dtype));
+    return p;
 }
 
 size_t ikbo_glm_mlp_workspace_size(int64_t num_cand, int64_t num_req, int32_t num_layers, const ikbo_glm_layer *layers,
@@ -637,6 +742,7 @@ size_t ikbo_glm_mlp_workspace_size(int64_t num_cand, int64_t num_req, int32_t nu
     cv.take(sizeof(float) * (size_t)(num_req > 0 ? num_req : 1) * (size_t)(max_nc > 0 ? max_nc : 1));
     cv.take(sizeof(float) * (size_t)smax * (size_t)(num_req > 0 ? num_req : 1) * (size_t)(max_ntot > 0 ? max_ntot : 1));
     cv.take(sizeof(int32_t) * (size_t)ikbo::lcb_fused_sync_ints(num_req > 0 ? num_req : 1, max_ntot > 0 ? max_ntot : 1));
+    carve_pads(cv, glm_pad_sizes(num_cand, num_req, num_layers, layers, in_dtype), nullptr);
     if (num_layers > 1) {
         const size_t e = esize(in_dtype);
         for (int b = 0; b < 2; ++b) {
@@ -647,12 +753,11 @@ size_t ikbo_glm_mlp_workspace_size(int64_t num_cand, int64_t num_req, int32_t nu
     return cv.used;
 }
 
-// The GLM-MLP with the last layer's outputs written with row strides ldo_r / ldo_c (0: packed).
-static int glm_mlp_impl(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
-                        const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
-                        int32_t num_layers, const ikbo_glm_layer *layers, int32_t in_dtype, int32_t out_dtype,
-                        void *y_req, void *y_cand, int64_t ldo_r, int64_t ldo_c, void *workspace,
-                        size_t workspace_bytes, void *hip_stream) {
+// Argument checks of the GLM-MLP (nothing enqueued)
+static int glm_mlp_check(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
+                         const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                         int32_t num_layers, const ikbo_glm_layer *layers, int32_t in_dtype, int32_t out_dtype,
+                         const void *y_req, const void *y_cand, const void *workspace, size_t workspace_bytes) {
     const int64_t C = num_cand, R = num_req;
     if (C < 0 || R < 0) return fail(IKBO_INVALID_ARGUMENT, "negative num_cand / num_req");
     if (num_layers <= 0 || !layers) return fail(IKBO_INVALID_ARGUMENT, "need num_layers >= 1 and a host layer array");
@@ -666,8 +771,6 @@ static int glm_mlp_impl(const void *x_req, int64_t num_req, const void *x_cand, 
         if (l > 0 && (ly.k_req != layers[l - 1].n_req_out || ly.k_cand != layers[l - 1].n_cand_out))
             return fail(IKBO_INVALID_ARGUMENT, "layer %d input widths (%d, %d) do not match layer %d outputs (%d, %d)", l,
                         ly.k_req, ly.k_cand, l - 1, layers[l - 1].n_req_out, layers[l - 1].n_cand_out);
-        if (l + 1 < num_layers && ((ly.n_req_out % (in_dtype == IKBO_F32 ? 4 : 8)) || (ly.n_cand_out % (in_dtype == IKBO_F32 ? 4 : 8))))
-            return fail(IKBO_MISALIGNED, "layer %d hidden widths must be multiples of 8 (bf16) / 4 (fp32)", l);
         const void *ptrs[] = {ly.w_rr, ly.w_cr, ly.w_cc, ly.b_r, ly.b_c};
         for (const void *p : ptrs)
             if (!aligned16(p)) return fail(IKBO_MISALIGNED, "layer %d: weight pointers must be 16-byte aligned", l);
@@ -685,7 +788,19 @@ static int glm_mlp_impl(const void *x_req, int64_t num_req, const void *x_cand, 
     const size_t need = ikbo_glm_mlp_workspace_size(C, R, num_layers, layers, in_dtype);
     if (workspace_bytes < need || !workspace)
         return fail(IKBO_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    return IKBO_OK;
+}
 
+// The GLM-MLP with the last layer's outputs written with row strides ldo_r / ldo_c (0: packed).
+static int glm_mlp_impl(const void *x_req, int64_t num_req, const void *x_cand, int64_t num_cand,
+                        const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                        int32_t num_layers, const ikbo_glm_layer *layers, int32_t in_dtype, int32_t out_dtype,
+                        void *y_req, void *y_cand, int64_t ldo_r, int64_t ldo_c, void *workspace,
+                        size_t workspace_bytes, void *hip_stream) {
+    const int64_t C = num_cand, R = num_req;
+    int rc = glm_mlp_check(x_req, R, x_cand, C, cand_to_req, req_cand_offsets, index_flags, num_layers, layers,
+                           in_dtype, out_dtype, y_req, y_cand, workspace, workspace_bytes);
+    if (rc) return rc;
     hipStream_t s = (hipStream_t)hip_stream;
     int32_t max_nr = 0, max_nc = 0, max_ntot = 0, smax = 1;
     for (int l = 0; l < num_layers; ++l) {
@@ -703,6 +818,7 @@ static int glm_mlp_impl(const void *x_req, int64_t num_req, const void *x_cand, 
     ws.partial = (float *)cv.take(sizeof(float) * ws.partial_cap);
     ws.sync_cap = ikbo::lcb_fused_sync_ints(R > 0 ? R : 1, max_ntot > 0 ? max_ntot : 1);
     ws.sync = (int32_t *)cv.take(sizeof(int32_t) * (size_t)ws.sync_cap);
+    carve_pads(cv, glm_pad_sizes(C, R, num_layers, layers, in_dtype), &ws);
     void *hr[2] = {nullptr, nullptr}, *hc[2] = {nullptr, nullptr};
     const size_t e = esize(in_dtype);
     if (num_layers > 1)
@@ -710,8 +826,9 @@ static int glm_mlp_impl(const void *x_req, int64_t num_req, const void *x_cand, 
             hr[b] = cv.take(e * (size_t)(R > 0 ? R : 1) * (size_t)(max_nr > 0 ? max_nr : 1));
             hc[b] = cv.take(e * (size_t)(C > 0 ? C : 1) * (size_t)(max_nc > 0 ? max_nc : 1));
         }
+    // the offsets, when given, define each candidate's request (as in every entry point)
     const int32_t *map = cand_to_req;
-    if (!map) {
+    if (req_cand_offsets) {
         IKBO_HIP(ikbo::launch_offsets_to_map(req_cand_offsets, R, C, ws.map, s));
         map = ws.map;
     }
@@ -792,9 +909,26 @@ int ikbo_dca_layer_forward(const void *x_req, int64_t num_req, const void *x_can
     const size_t att_bytes = workspace_bytes - cv.used;
     const int64_t ld = 2 * W;                                  // rows of [Q | A]
     char *a_req = (char *)y_req + W * e, *a_cand = (char *)y_cand + W * e;
+    // every stage's arguments are checked before the first launch, so an error other than
+    // IKBO_HIP_ERROR leaves the outputs untouched
+    int rc = glm_mlp_check(x_req, R, x_cand, C, cand_to_req, req_cand_offsets, index_flags, num_glm_layers, glm_layers,
+                           dtype, dtype, y_req, y_cand, ws_glm, g_bytes);
+    if (rc) return rc;
+    if (R > 0) {
+        const int32_t hd = num_heads * head_dim;
+        rc = kv_project_check(seq, seq_rows, seq_dim, w_k_cand, w_v_cand, hd, dtype, dtype, kbuf, vbuf);
+        if (!rc) rc = kv_project_check(seq, seq_rows, seq_dim, w_k_req, w_v_req, hd, dtype, dtype, kbuf, vbuf);
+        if (!rc && C > 0)
+            rc = dca_validate(y_cand, C, q_len, kbuf, vbuf, R, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets,
+                              index_flags, num_heads, head_dim, dtype, dtype, a_cand, ws_att, att_bytes);
+        if (!rc)
+            rc = request_attention_check(y_req, R, q_len, kbuf, vbuf, kv_cu_seqlens, kv_len, num_heads, head_dim, dtype,
+                                         dtype, a_req, ws_att, att_bytes);
+        if (rc) return rc;
+    }
     // Eq. 12: the query generator (LCB_i and MLP_i), its outputs in the left halves
-    int rc = glm_mlp_impl(x_req, R, x_cand, C, cand_to_req, req_cand_offsets, index_flags, num_glm_layers, glm_layers,
-                          dtype, dtype, y_req, y_cand, ld, ld, ws_glm, g_bytes, hip_stream);
+    rc = glm_mlp_impl(x_req, R, x_cand, C, cand_to_req, req_cand_offsets, index_flags, num_glm_layers, glm_layers,
+                      dtype, dtype, y_req, y_cand, ld, ld, ws_glm, g_bytes, hip_stream);
     if (rc) return rc;
     if (R == 0) {
         // no request: every candidate's attention half is zero (no valid request)
@@ -806,9 +940,6 @@ int ikbo_dca_layer_forward(const void *x_req, int64_t num_req, const void *x_can
                          hip_stream);
     if (rc) return rc;
     if (C > 0) {
-        rc = dca_validate(y_cand, C, q_len, kbuf, vbuf, R, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets,
-                          index_flags, num_heads, head_dim, dtype, dtype, a_cand, ws_att, att_bytes);
-        if (rc) return rc;
         rc = dca_run(y_cand, C, q_len, kbuf, vbuf, R, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets, num_heads,
                      head_dim, softmax_scale, dtype, dtype, a_cand, ws_att, (hipStream_t)hip_stream, ld, ld);
         if (rc) return rc;

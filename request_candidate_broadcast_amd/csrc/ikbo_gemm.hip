@@ -786,6 +786,27 @@ __global__ void splitk_reduce_kernel(const float *partial, int32_t splits, int64
     }
 }
 
+// Zero-padded copy of bf16 rows (the alignment rule of Sec. 4.2.4): dst[r, j] = src[r, j] for j < k
+// and 0 for k <= j < kp, with src rows k elements long and dst rows kp (a multiple of 8). One
+// thread per 16-byte chunk of a destination row; the source rows are not 16-byte aligned, so their
+// elements are read one by one.
+__global__ void pad_rows_bf16_kernel(const uint16_t *src, int64_t rows, int32_t k, uint16_t *dst, int32_t kp) {
+    const int64_t chunks = kp / 8, total = rows * chunks;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / chunks;
+        const int32_t j0 = (int32_t)(i - r * chunks) * 8;
+        const uint16_t *sp = src + r * k;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = j0 + 2 * e < k ? sp[j0 + 2 * e] : 0u;
+            const uint32_t hi = j0 + 2 * e + 1 < k ? sp[j0 + 2 * e + 1] : 0u;
+            w[e] = lo | (hi << 16);
+        }
+        *(uint4 *)(dst + r * kp + j0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 // ----------------------------------------------------------------------------------------------
 // Persistent LCB layer (request/candidate co-scheduling, ROCS Sec. 4.2.3). sync layout (int32):
 // [0] request item counter, [1 .. 8] candidate tile counter of each XCD, [9] wait ran out,
@@ -1092,6 +1113,16 @@ hipError_t launch_lcb_fused(const LcbFusedArgs &f, hipStream_t s) {
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
     if (out_staging_ok(f.cand)) hipLaunchKernelGGL((lcb_fused_kernel<true, true, true>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, f);
     else hipLaunchKernelGGL((lcb_fused_kernel<true, true, false>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, f);
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_rows_bf16(const void *src, int64_t rows, int32_t k, void *dst, int32_t kp, hipStream_t s) {
+    const int64_t total = rows * (int64_t)(kp / 8);
+    if (total <= 0) return hipSuccess;
+    int64_t g = (total + 255) / 256;
+    if (g > 65536) g = 65536;
+    hipLaunchKernelGGL(pad_rows_bf16_kernel, dim3((unsigned)g), dim3(256), 0, s, (const uint16_t *)src, rows, k,
+                       (uint16_t *)dst, kp);
     return hipGetLastError();
 }
 

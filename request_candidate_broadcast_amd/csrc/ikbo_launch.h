@@ -20,10 +20,15 @@ hipError_t launch_histogram(const int32_t *m, int64_t C, int64_t R, int32_t *cou
 hipError_t launch_scan_tiles(const int32_t *counts, const int32_t *off_in, int64_t R, int64_t C, int32_t q_len,
                              int32_t heads, int32_t block_m, int32_t *off_out, int32_t *cursor,
                              int32_t *tile_start, hipStream_t s);
-// perm[cursor[m[c]]++] = c for valid m; rows of candidates with invalid m are zeroed in `out`
-// (row_elems elements of out_bytes each, rows row_stride elements apart).
-hipError_t launch_scatter(const int32_t *m, int64_t C, int64_t R, int32_t *cursor, int32_t *perm, void *out,
-                          int64_t row_elems, int64_t row_stride, int out_bytes, hipStream_t s);
+// Stable grouping of an arbitrary map: perm lists the candidates with a valid request sorted by
+// request, each request's candidates in increasing index order, then those without one. scratch
+// holds stable_group_scratch_ints(C) int32.
+int64_t stable_group_scratch_ints(int64_t C);
+hipError_t launch_stable_group(const int32_t *m, int64_t C, int64_t R, int32_t *perm, int32_t *scratch, hipStream_t s);
+// Rows of `out` of candidates whose m is outside [0, R) are zeroed (row_elems elements of out_bytes
+// each, rows row_stride elements apart).
+hipError_t launch_zero_invalid_rows(const int32_t *m, int64_t C, int64_t R, void *out, int64_t row_elems,
+                                    int64_t row_stride, int out_bytes, hipStream_t s);
 // m_out[c] = r with off[r] <= c < off[r+1] (binary search over a sanitised view), -1 when none.
 hipError_t launch_offsets_to_map(const int32_t *off, int64_t R, int64_t C, int32_t *m_out, hipStream_t s);
 // Zero rows of `out` for candidates outside [clamp(off[0]), clamp(off[R])) (row_elems elements,
@@ -83,6 +88,9 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
 hipError_t launch_splitk_reduce(const float *partial, int32_t splits, int64_t M, int32_t N, int32_t n_split,
                                 const float *bias0, int32_t act, void *out0, int32_t out0_f32, int64_t ld0,
                                 float *out1, hipStream_t s);
+// Zero-padded copy of bf16 rows: dst [rows, kp] (kp a multiple of 8, 16-byte aligned) holds src
+// [rows, k] (any k <= kp) in its first k columns and zeros after them.
+hipError_t launch_pad_rows_bf16(const void *src, int64_t rows, int32_t k, void *dst, int32_t kp, hipStream_t s);
 // Split count the request GEMM uses for an M x N x K problem.
 int32_t request_gemm_splits(int64_t M, int32_t N, int32_t K, int in_f32);
 

@@ -54,7 +54,13 @@ def test_workspace_sizes(lib):
     assert lib.ikbo_dca_workspace_size(1000, 10) >= 4 * (1000 + 3 * 11)
     assert lib.ikbo_dca_workspace_size(-1, 10) == 0
     # Z in fp32 [R, N_c] at least
-    assert lib.ikbo_lcb_workspace_size(100, 8, 64, 32, 48) >= 4 * 8 * 48
+    assert lib.ikbo_lcb_workspace_size(100, 8, 64, 64, 32, 48, 1) >= 4 * 8 * 48
+    assert lib.ikbo_lcb_workspace_size(100, 8, 64, 64, 32, 48, 7) == 0
+    # a misaligned bf16 K width adds zero-padded copies of the operands it multiplies
+    aligned = lib.ikbo_lcb_workspace_size(100, 8, 64, 64, 32, 48, 1)
+    padded = lib.ikbo_lcb_workspace_size(100, 8, 64, 61, 32, 48, 1)
+    assert padded >= aligned + 2 * 64 * (100 + 48)
+    assert lib.ikbo_lcb_workspace_size(100, 8, 64, 61, 32, 48, 0) == lib.ikbo_lcb_workspace_size(100, 8, 64, 64, 32, 48, 0)
     layers = (ikbo.GlmLayer * 2)()
     layers[0] = ikbo.GlmLayer(None, None, None, None, None, 64, 32, 48, 40, 1)
     layers[1] = ikbo.GlmLayer(None, None, None, None, None, 48, 40, 16, 24, 0)
@@ -107,8 +113,9 @@ def lcb(lib, **kw):
 
 def test_lcb_argument_errors(lib):
     assert lcb(lib, m=None, off=None) == ikbo.IKBO_INVALID_ARGUMENT
-    assert lcb(lib, kr=60) == ikbo.IKBO_MISALIGNED          # bf16 rows must be 16-byte multiples
-    assert lcb(lib, ind=0, kr=62) == ikbo.IKBO_MISALIGNED   # fp32: multiples of 4 elements
+    # misaligned K widths are padded in the workspace: its size, not the width, is checked
+    need = lib.ikbo_lcb_workspace_size(32, 4, 60, 64, 32, 32, 1)
+    assert lcb(lib, kr=60, wsb=need - 1) == ikbo.IKBO_WORKSPACE_TOO_SMALL
     assert lcb(lib, act=5) == ikbo.IKBO_INVALID_ARGUMENT
     assert lcb(lib, nr=-1) == ikbo.IKBO_INVALID_ARGUMENT
     assert lcb(lib, wcc=None) == ikbo.IKBO_INVALID_ARGUMENT
@@ -135,7 +142,9 @@ def test_glm_mlp_argument_errors(lib):
     odd = (ikbo.GlmLayer * 2)()
     odd[0] = ikbo.GlmLayer(FAKE, FAKE, FAKE, None, None, 64, 32, 44, 40, 1)   # hidden width not a multiple of 8
     odd[1] = ikbo.GlmLayer(FAKE, FAKE, FAKE, None, None, 44, 40, 16, 24, 0)
-    assert f(ly=odd) == ikbo.IKBO_MISALIGNED
+    need_odd = lib.ikbo_glm_mlp_workspace_size(32, 4, 2, odd, 1)
+    assert need_odd > lib.ikbo_glm_mlp_workspace_size(32, 4, 2, layers, 1)   # room for the padded copies
+    assert f(ly=odd, wsb=need_odd - 1) == ikbo.IKBO_WORKSPACE_TOO_SMALL
 
 
 def test_check_index_argument_errors(lib):
@@ -270,3 +279,17 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.ikbo_probe_launch(0, FAKE, 1000, 10, 4, None) == 1             # output too small
     assert lib.ikbo_probe_launch(9, FAKE, 1 << 20, 10, 4, None) == 1          # unknown probe
     assert lib.ikbo_probe_launch(2, FAKE + 4, 1 << 20, 0, 4, None) == 1       # misaligned copy
+
+
+def test_dca_layer_checks_every_stage_before_launching(lib):
+    # bf16 attention is built for head_dim 64 and 128. With 96 the call must fail before the query
+    # generator is launched; without a GPU a launch would report IKBO_HIP_ERROR instead.
+    W = 4 * 2 * 96
+    layers = (ikbo.GlmLayer * 1)()
+    layers[0] = ikbo.GlmLayer(FAKE, FAKE, FAKE, None, None, 64, 64, W, W, 0)
+    need = lib.ikbo_dca_layer_workspace_size(32, 4, 1, layers, 64, 2, 96, 1)
+    assert need > 0
+    rc = lib.ikbo_dca_layer_forward(FAKE, 4, FAKE, 32, FAKE, None, 0, 1, layers, FAKE, 64, 128, None, 16, FAKE, FAKE,
+                                    FAKE, FAKE, 4, 2, 96, 0.0, 1, FAKE, FAKE, FAKE, need, None)
+    assert rc == ikbo.IKBO_UNSUPPORTED, lib.ikbo_last_error_message()
+    assert b"head_dim" in lib.ikbo_last_error_message()

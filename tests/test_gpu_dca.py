@@ -125,16 +125,17 @@ def test_invalid_map_rows_are_zero():
 
 
 def test_single_key_is_exact():
-    # P2: L_r = 1 -> softmax weight 1 -> O == V[r, 0]. The kernel folds the softmax scale into one
-    # FMA, so the weight of the max key is exp2 of that product's rounding residual (|x| < 2^-20):
-    # the fp32 output is within a few ulp of V and the bf16 output equals V bit for bit.
+    # P2: L_r = 1 -> softmax weight 1 -> O == V[r, 0], bit for bit in both output dtypes. The kernel
+    # folds the softmax scale into one FMA, so the weight of the max key is exp2 of that product's
+    # rounding residual (|x| < 2^-20); its bf16 rounding, the value the PV product and the row sum
+    # both use, is exactly 1, so O = V * 1 / 1.
     counts = [33, 300, 2]
     s, q, k, v = make_case(42, counts, [1, 1, 1], 2, 128, 1, "bf16")
     note("dca single key")
     got = run_gpu(s, q, k, v)
     vv = synth.bf16_to_f64(v.reshape(3, 2, 128))
     want = vv[s.cand_to_req][:, None]
-    np.testing.assert_allclose(down_f64(got), want, rtol=2 ** -20, atol=0)
+    assert np.array_equal(down_f64(got), want)
     got16 = run_gpu(s, q, k, v, out_dtype=torch.bfloat16)
     assert np.array_equal(bf16_bits(got16), v.reshape(3, 2, 128)[s.cand_to_req][:, None])
 
@@ -148,7 +149,7 @@ def test_request_tag_exact():
     note("dca request tag")
     got = run_gpu(s, q, k, vt)
     want = np.broadcast_to(s.cand_to_req[:, None, None, None].astype(np.float64), tuple(got.shape))
-    np.testing.assert_allclose(down_f64(got), want, rtol=2 ** -20, atol=0)
+    assert np.array_equal(down_f64(got), want)
     got16 = run_gpu(s, q, k, vt, out_dtype=torch.bfloat16)
     assert np.array_equal(down_f64(got16), want)
 

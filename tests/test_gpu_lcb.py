@@ -210,3 +210,42 @@ def test_mlp_bf16_three_layers_and_closure():
     assert torch.equal(y_r, y_r2)
     y_r16, y_c16 = run_mlp(x_r, x_c, layers, m=m, out_dtype=torch.bfloat16)
     assert np.array_equal(bf16_bits(y_c16), rne_bits_of(y_c))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ks", [(100, 262), (262, 1001), (1001, 100), (7, 3)])
+def test_misaligned_k_widths(dtype, ks):
+    # B5, the alignment rule (Sec. 4.2.4): K widths that break 16-byte rows are zero-padded inside
+    # the call (bf16) or read element by element (fp32); the results meet the same bars
+    k_req, k_cand = ks
+    counts = np.array([2, 130, 0, 41])
+    R, C = len(counts), int(counts.sum())
+    x_r, x_c = make_x(15, R, C, k_req, k_cand, dtype)
+    ly = make_layer(15, k_req, k_cand, 72, 200, dtype, "gelu")
+    m = synth.cand_to_req_from_counts(counts)
+    note("lcb misaligned k=%s %s" % (ks, dtype))
+    y_r, y_c = run_lcb(x_r, x_c, ly, m=m)
+    want = oracle.glm(x_r, x_c, [ly], m=m, want_request=True)
+    assert_parity(down_f64(y_c), want["y_c"], dtype, "y_c")
+    assert_parity(down_f64(y_r), want["y_r"], dtype, "y_r")
+    if dtype == "bf16":
+        y_r16, y_c16 = run_lcb(x_r, x_c, ly, m=m, out_dtype=torch.bfloat16)
+        assert np.array_equal(bf16_bits(y_c16), rne_bits_of(y_c))
+        assert np.array_equal(bf16_bits(y_r16), rne_bits_of(y_r))
+
+
+def test_mlp_misaligned_input_and_hidden_widths():
+    # every layer pads its own misaligned inputs, hidden widths included
+    counts = np.array([3, 200, 5])
+    R, C = 3, 208
+    x_r, x_c = make_x(16, R, C, 100, 262, "bf16")
+    layers = [make_layer(16, 100, 262, 44, 52, "bf16", "gelu", base=20),
+              make_layer(16, 44, 52, 36, 30, "bf16", "none", base=30)]
+    m = synth.cand_to_req_from_counts(counts)
+    note("mlp bf16 misaligned widths")
+    y_r, y_c = run_mlp(x_r, x_c, layers, m=m)
+    want = oracle.glm(x_r, x_c, layers, m=m, want_request=True)
+    assert_parity(down_f64(y_c), want["y_c"], "bf16", "mlp y_c")
+    assert_parity(down_f64(y_r), want["y_r"], "bf16", "mlp y_r")
+    y_r16, y_c16 = run_mlp(x_r, x_c, layers, m=m, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_bits(y_c16), rne_bits_of(y_c))
