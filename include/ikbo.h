@@ -113,6 +113,31 @@ int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len,
                      void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* ------------------------------------------------------------------------------------------
+ * IKBO-DCA without allocation, for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors are those of ikbo_dca_forward (same kernels, same bits); the
+ * scratch that call takes from `workspace` comes instead from a fixed array of
+ * IKBO_DCA_NOALLOC_SCRATCH_BYTES bytes that the library keeps on every GPU it runs on, from the
+ * first call on that GPU until the process ends. The first call on a device looks the array up
+ * (hipGetSymbolAddress, on the current device); no call allocates. Uses the current device's
+ * array: hip_stream must belong to the current device.
+ * Limit: ikbo_dca_workspace_size(num_cand, num_req) must not exceed the array (about 1.5 million
+ *        candidates); larger calls return IKBO_WORKSPACE_TOO_SMALL and enqueue nothing.
+ * Calls that overlap on one GPU (on different streams, or from different host threads without
+ * stream ordering) share that array and race; calls ordered on one stream do not. Every call sets
+ * up the parts of the array it reads (counters are cleared by kernels), so no state carries over
+ * from a previous call.
+ * ---------------------------------------------------------------------------------------- */
+#define IKBO_DCA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int ikbo_dca_forward_noalloc(const void *q, int64_t num_cand, int32_t q_len,
+                             const void *k, const void *v, int64_t num_req,
+                             const int32_t *kv_cu_seqlens, int32_t kv_len,
+                             const int32_t *cand_to_req, const int32_t *req_cand_offsets, uint32_t index_flags,
+                             int32_t num_heads, int32_t head_dim, float softmax_scale,
+                             int32_t in_dtype, int32_t out_dtype, void *out, void *hip_stream);
+
+/* ------------------------------------------------------------------------------------------
  * IKBO-LCB: the GLM-masked two-group linear layer (Sec. 3.1.2, Eq. 4 with the mask of Eq. 3,
  * block form Eq. 6), run as the decomposition of Sec. 4.1, Eq. 14:
  *   [y_r ; Z] = [W_RR ; W_CR] x_r          once per request (request batch),

@@ -29,6 +29,7 @@ IKBO_F32, IKBO_BF16 = 0, 1
 IKBO_ACT_NONE, IKBO_ACT_GELU = 0, 1
 IKBO_INDEX_SORTED = 1
 IKBO_NORM_NONE, IKBO_NORM_LAYER, IKBO_NORM_RMS = 0, 1, 2
+IKBO_DCA_NOALLOC_SCRATCH_BYTES = 32 << 20      # the fixed scratch array of ikbo_dca_forward_noalloc
 
 ACTIVATIONS = {"none": IKBO_ACT_NONE, "gelu": IKBO_ACT_GELU, None: IKBO_ACT_NONE}
 
@@ -58,7 +59,7 @@ EXPORTS = ["ikbo_version", "ikbo_status_string", "ikbo_last_error_message",
            "ikbo_glm_mlp_workspace_size", "ikbo_glm_mlp_forward", "ikbo_check_index",
            "ikbo_kv_project", "ikbo_request_attention_workspace_size", "ikbo_request_attention",
            "ikbo_fm_forward", "ikbo_lcb_emb_workspace_size", "ikbo_lcb_emb_forward",
-           "ikbo_dca_layer_workspace_size", "ikbo_dca_layer_forward"]
+           "ikbo_dca_layer_workspace_size", "ikbo_dca_layer_forward", "ikbo_dca_forward_noalloc"]
 
 _lib = None
 
@@ -111,6 +112,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ikbo_dca_forward.restype = ctypes.c_int
     lib.ikbo_dca_forward.argtypes = [vp, i64, i32, vp, vp, i64, vp, i32, vp, vp, u32, i32, i32, f32, i32, i32, vp,
                                      vp, sz, vp]
+    lib.ikbo_dca_forward_noalloc.restype = ctypes.c_int
+    lib.ikbo_dca_forward_noalloc.argtypes = [vp, i64, i32, vp, vp, i64, vp, i32, vp, vp, u32, i32, i32, f32, i32, i32,
+                                             vp, vp]
     lib.ikbo_lcb_workspace_size.restype = sz
     lib.ikbo_lcb_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32, i32]
     lib.ikbo_lcb_forward.restype = ctypes.c_int

@@ -10,6 +10,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <mutex>
 #include <string>
 
 namespace {
@@ -461,6 +462,60 @@ int ikbo_dca_forward(const void *q, int64_t num_cand, int32_t q_len, const void 
     if (rc) return rc;
     return dca_run(q, num_cand, q_len, k, v, num_req, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets, num_heads,
                    head_dim, softmax_scale, in_dtype, out_dtype, out, workspace, (hipStream_t)hip_stream);
+}
+
+// ---- IKBO-DCA without allocation ------------------------------------------------------------------
+// Scratch for callers that cannot allocate: one fixed array on every GPU the library runs on, held
+// until the process ends. In host code `scratch` is a host-side stand-in for the symbol, not a
+// device address: its device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[IKBO_DCA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];     // device address of `scratch` on each device, once looked up
+
+// The device address of the current device's scratch array (looked up on its first use).
+int current_device_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(IKBO_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(IKBO_HIP_ERROR, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return IKBO_OK;
+}
+}  // namespace
+
+int ikbo_dca_forward_noalloc(const void *q, int64_t num_cand, int32_t q_len, const void *k, const void *v,
+                             int64_t num_req, const int32_t *kv_cu_seqlens, int32_t kv_len, const int32_t *cand_to_req,
+                             const int32_t *req_cand_offsets, uint32_t index_flags, int32_t num_heads,
+                             int32_t head_dim, float softmax_scale, int32_t in_dtype, int32_t out_dtype, void *out,
+                             void *hip_stream) {
+    if (num_cand < 0 || num_req < 0)
+        return fail(IKBO_INVALID_ARGUMENT, "bad sizes (num_cand %lld num_req %lld)", (long long)num_cand,
+                    (long long)num_req);
+    const size_t need = ikbo_dca_workspace_size(num_cand, num_req);
+    if (need > (size_t)IKBO_DCA_NOALLOC_SCRATCH_BYTES)
+        return fail(IKBO_WORKSPACE_TOO_SMALL, "num_cand %lld / num_req %lld need %zu bytes of scratch, above the fixed "
+                    "%zu-byte array of ikbo_dca_forward_noalloc (use ikbo_dca_forward with a workspace)",
+                    (long long)num_cand, (long long)num_req, need, (size_t)IKBO_DCA_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    int rc = current_device_scratch(&ws);
+    if (rc) return rc;
+    rc = dca_validate(q, num_cand, q_len, k, v, num_req, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets,
+                      index_flags, num_heads, head_dim, in_dtype, out_dtype, out, ws, IKBO_DCA_NOALLOC_SCRATCH_BYTES);
+    if (rc) return rc;
+    return dca_run(q, num_cand, q_len, k, v, num_req, kv_cu_seqlens, kv_len, cand_to_req, req_cand_offsets, num_heads,
+                   head_dim, softmax_scale, in_dtype, out_dtype, out, ws, (hipStream_t)hip_stream);
 }
 
 // ---- request-side attention ---------------------------------------------------------------------
