@@ -160,6 +160,13 @@ int ikbo_dca_forward_noalloc(const void *q, int64_t num_cand, int32_t q_len,
  * workspace >= ikbo_lcb_workspace_size(num_cand, num_req, k_req, k_cand, n_req_out, n_cand_out,
  *       in_dtype) bytes; it holds the candidate->request map built from the offsets, Z in fp32,
  *       the request GEMM's split-K partial sums and, for misaligned bf16 K widths, the padded copies.
+ * Environment: IKBO_LCB_FUSED=1 runs a bf16 layer as one persistent launch in which request and
+ *       candidate tiles share the schedule (Sec. 4.2.3: request items claimed ascending, candidate
+ *       tiles descending; each candidate epilogue waits on the ready flags of the request tiles
+ *       holding its Z columns). Same results bit for bit; two launches are the default, being
+ *       faster on MI355X. Each wait is bounded (0.5 s); a wait that runs out writes the tile as NaN.
+ *       IKBO_LCB_FUSED_WAIT_NS sets that bound in nanoseconds; a negative value also keeps the
+ *       request tiles from setting their flags (a host-forced test of the bounded waits).
  * ---------------------------------------------------------------------------------------- */
 size_t ikbo_lcb_workspace_size(int64_t num_cand, int64_t num_req, int32_t k_req, int32_t k_cand,
                                int32_t n_req_out, int32_t n_cand_out, int32_t in_dtype);

@@ -253,6 +253,15 @@ int run_lcb(const void *x_req, int64_t R, int32_t k_req, const void *x_cand, int
         f.out0_f32 = out_dtype == IKBO_F32;
         f.sync = ws.sync;
         f.wait_ticks = ikbo::wall_clock_ticks(0.5);   // a safety bound, never reached when the request tiles run
+        f.publish = 1;
+        // IKBO_LCB_FUSED_WAIT_NS: the bound in nanoseconds instead; a negative value also keeps the
+        // request tiles from setting their ready flags, so every candidate wait gives up after
+        // |value| ns (a host-forced test of the timeout path: the launch still ends, with NaN tiles)
+        if (const char *w = getenv("IKBO_LCB_FUSED_WAIT_NS")) {
+            const long long ns = atoll(w);
+            f.wait_ticks = ikbo::wall_clock_ticks((double)(ns < 0 ? -ns : ns) * 1e-9);
+            f.publish = ns >= 0;
+        }
         if ((size_t)R * (size_t)g.N <= ws.partial_cap && ws.sync_cap >= ikbo::lcb_fused_sync_ints(R, g.N) &&
             ikbo::lcb_fused_supported(g, h)) {
             IKBO_HIP(ikbo::launch_lcb_fused(f, s));

@@ -16,6 +16,8 @@
 // The request GEMM ([Y_r | Z] = x_r [W_RR; W_CR]^T, a small M = num_req) runs split-K into fp32
 // partial sums, reduced in a fixed order by a second kernel that also applies the request-group
 // epilogue; results are deterministic.
+#include <type_traits>
+
 #include "ikbo_device.h"
 #include "ikbo_launch.h"
 
@@ -212,9 +214,20 @@ struct NoHook {
     __device__ void operator()() const {}
 };
 
+// The mark of an output tile whose result is not available: NaN in columns col..col+3 below N.
+__device__ __forceinline__ void store_nan4(const GemmArgs &a, int64_t row, int64_t col) {
+    for (int e = 0; e < 4; ++e)
+        if (col + e < a.N) {
+            if (a.out_f32) ((float *)a.out)[row * a.ldo + col + e] = __builtin_nanf("");
+            else ((uint16_t *)a.out)[row * a.ldo + col + e] = 0x7fc0;
+        }
+}
+
 // One output tile (mt, nt) over the k range of split sp. sx[s] / sw[s] are the LDS stages of the
 // activation / weight tiles (the caller's __shared__ arrays, one per stage). pre_epilogue() runs
-// between the main loop and the epilogue (every thread), mid_epilogue() once inside the epilogue,
+// between the main loop and the epilogue (every thread); when it returns a bool, false (the same
+// in every thread) makes the epilogue store the NaN mark in every output element of the tile
+// instead of its result, reading neither bias nor Z. mid_epilogue() runs once inside the epilogue,
 // after the loads of its first column group are issued (LDS is free by then: a copy issued there
 // does not delay those loads, which it would when issued before them). prefetched: the caller has
 // already copied step 0 into stage 0 with dma_fetch (direct copies, two stages).
@@ -381,7 +394,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
         }
     }
 
-    pre_epilogue();
+    bool mark = false;
+    if constexpr (std::is_same_v<decltype(pre_epilogue()), bool>) mark = !pre_epilogue();
+    else pre_epilogue();
 
     // ---- epilogue ----
     // Fast form, uniform per tile: every column of the tile inside N and 16-byte output / Z rows.
@@ -528,6 +543,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
 #pragma unroll
                             for (int e = 0; e < 16; ++e) v[j][e] = rok[j] ? v[j][e] : 0.0f;
                     }
+                    if (mark) {
+#pragma unroll
+                        for (int j = 0; j < MB; ++j)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) v[j][e] = __builtin_nanf("");
+                    }
                     if constexpr (STG) {
                         const int sw7 = (l32 >> 1) & 7, hs = half ^ ((l32 >> 4) & 1);
                         if (a.out_f32) {
@@ -570,7 +591,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
             };
             const std::true_type T;
             const std::false_type F;
-            if (a.bias) {
+            if (mark) {
+                body(F, F, F);
+            } else if (a.bias) {
                 if (!a.z) body(T, F, F);
                 else if (zcoh) body(T, T, T);
                 else body(T, T, F);
@@ -597,6 +620,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int mt, int nt, int
                     for (int e = 0; e < 4; ++e)
                         if (col + e < a.N) pp[col + e] = acc[i][j][4 * jj + e];
                 }
+        } else if (mark) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) store_nan4(a, row, n0 + wn * TN + i * 32 + 8 * jj + 4 * half);
         } else {
             int64_t zrow;
             const bool ok = row_request(a, row, zrow);
@@ -863,7 +891,10 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
     using CG = GemmShape<kWGM, kWGN, kTM, kTN, BK>;
 
     // wave 0 claims the next item (request items first, then this XCD's candidate tiles) and
-    // hands it to the workgroup through LDS
+    // hands it to the workgroup through LDS. Bidirectional order (Sec. 4.2.3): request items go
+    // out ascending from one device-wide counter, candidate tiles descending from the end of each
+    // XCD's range (with claims the balance comes from the claims themselves; the order is the
+    // pages').
     auto claim = [&]() -> int64_t {
         if (wave == 0) {
             int64_t it = -1;
@@ -871,8 +902,8 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
             if (r < req_items) {
                 it = r;
             } else {
-                const int64_t c = c_beg + lane0(lane, [&] { return atomicAdd(&f.sync[1 + xcd], 1); });
-                if (c < c_end) it = req_items + c;
+                const int64_t c = c_end - 1 - lane0(lane, [&] { return atomicAdd(&f.sync[1 + xcd], 1); });
+                if (c >= c_beg) it = req_items + c;
             }
             if (lane == 0) s_item = it;
         }
@@ -928,7 +959,7 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
                 }
                 wait_vmcnt<0>();                   // Z and Y_r have reached the L2 ...
                 __syncthreads();
-                if (wave == 0 && lane == 0) flag_release(&ready[tile], 1);   // ... memory, then the flag
+                if (wave == 0 && lane == 0 && f.publish) flag_release(&ready[tile], 1);   // ... memory, then the flag
             }
             item = claim();
             prefetched = false;
@@ -965,14 +996,15 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
                             }
                             if (ok && ti < 64) known |= 1ull << ti;
                         }
-                    const int64_t c2 = c_beg + lane0(lane, [&] { return atomicAdd(&f.sync[1 + xcd], 1); });
+                    const int64_t c2 = c_end - 1 - lane0(lane, [&] { return atomicAdd(&f.sync[1 + xcd], 1); });
                     if (lane == 0) {
                         s_flag = ok;
-                        s_item = c2 < c_end ? req_items + c2 : -1;
+                        s_item = c2 >= c_beg ? req_items + c2 : -1;
                     }
                 }
                 __syncthreads();
                 next = uniform64(s_item);
+                return __builtin_amdgcn_readfirstlane(s_flag) != 0;
             };
             auto mid = [&] {
                 if constexpr (DMA_C) {
@@ -986,18 +1018,10 @@ __global__ __launch_bounds__(kGemmThreads) void lcb_fused_kernel(LcbFusedArgs f)
             // the epilogue reads Z with plain loads when its lines hold one request tile each, else
             // with coherent loads; no acquire fence, which would invalidate the XCD's L2 (and the
             // weight and activation tiles the other workgroups there hold) per tile
+            // when a wait ran out, pre returns false and the epilogue marks the whole tile NaN without
+            // reading Z: a line of Z read before its tile is final could otherwise stay in this XCD's
+            // L2 and reach a later tile's plain loads
             gemm_tile<kWGM, kWGN, kTM, kTN, BK, 2, DMA_C, false, true, STG>(cd, mt, nt, 0, cd.K, sx, sw, pre, prefetched, mid);
-            if (!__builtin_amdgcn_readfirstlane(s_flag)) {
-                // the wait ran out: mark the tile's rows as invalid output
-                for (int i = tid; i < BM * BN; i += kGemmThreads) {
-                    const int64_t row = (int64_t)mt * BM + i / BN;
-                    const int col = nt * BN + i % BN;
-                    if (row < cd.M && col < cd.N) {
-                        if (cd.out_f32) ((float *)cd.out)[row * cd.ldo + col] = __builtin_nanf("");
-                        else ((uint16_t *)cd.out)[row * cd.ldo + col] = 0x7fc0;
-                    }
-                }
-            }
             item = next;
             prefetched = DMA_C && next >= 0;
         }

@@ -112,6 +112,8 @@ struct LcbFusedArgs {
     int32_t *sync;          // lcb_fused_sync_ints(...) int32, zeroed by launch_lcb_fused
     int64_t wait_ticks;     // bound on each flag wait, in ticks of the device's constant wall clock;
                             // a wait that runs out sets sync[9] and poisons the tile's output with NaN
+    int32_t publish;        // 1: request tiles set their ready flags; 0 (a test of the bounded
+                            // waits, set from the host): they never do, so every wait gives up
 };
 // ticks of the device's constant wall clock (wall_clock64) in the given number of seconds
 int64_t wall_clock_ticks(double seconds);

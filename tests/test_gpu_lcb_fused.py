@@ -96,3 +96,63 @@ def test_fused_repeated_calls_reuse_the_workspace():
         os.environ.pop("IKBO_LCB_FUSED", None)
     for yr, yc in outs[1:]:
         assert same_bits(yc, outs[0][1]) and same_bits(yr, outs[0][0])
+
+
+def fused_with_wait_bound(ns, fn):
+    os.environ["IKBO_LCB_FUSED"] = "1"
+    os.environ["IKBO_LCB_FUSED_WAIT_NS"] = str(ns)
+    try:
+        return fn()
+    finally:
+        os.environ.pop("IKBO_LCB_FUSED", None)
+        os.environ.pop("IKBO_LCB_FUSED_WAIT_NS", None)
+
+
+def test_bounded_waits_give_up_with_nan_tiles():
+    """The candidate epilogue's wait on the request tiles' ready flags is bounded in time. Forced
+    from the host (IKBO_LCB_FUSED_WAIT_NS < 0: the request tiles withhold their flags, the bound is
+    2 us), every wait gives up, the launch still ends, every candidate output is NaN (the documented
+    mark), and the request-group output, which needs no flag, is the two-launch result. A normal
+    launch on the same workspace afterwards is bit-equal to the two-launch form again."""
+    R, C = len(COUNTS), int(COUNTS.sum())
+    x_r, x_c = make_x(24, R, C, 256, 128, "bf16")
+    ly = make_layer(24, 256, 128, 256, 512, "bf16", "gelu")
+    m = synth.cand_to_req_from_counts(COUNTS)
+    note("lcb fused: withheld flags, 2 us wait bound")
+    ref_r, ref_c = run_lcb(x_r, x_c, ly, m=m)
+    yr, yc = fused_with_wait_bound(-2000, lambda: run_lcb(x_r, x_c, ly, m=m))
+    assert torch.isnan(yc).all()
+    assert same_bits(yr, ref_r)
+    note("lcb fused: normal launch after the forced timeouts")
+    os.environ["IKBO_LCB_FUSED"] = "1"
+    try:
+        yr2, yc2 = run_lcb(x_r, x_c, ly, m=m)
+    finally:
+        os.environ.pop("IKBO_LCB_FUSED", None)
+    assert same_bits(yc2, ref_c) and same_bits(yr2, ref_r)
+
+
+@pytest.mark.parametrize("wait_ns", [0, 4000, 40000])
+def test_short_wait_bounds_mark_whole_tiles_only(wait_ns):
+    """With a short bound and published flags, a candidate tile whose flags are not set within the
+    bound gives up (and, once one has, every later wait stops at once): each 256 x 256 output tile
+    is then either bit-equal to the two-launch result or NaN throughout (no partly written tile)."""
+    R, C = 700, 2600
+    x_r, x_c = make_x(25, R, C, 2048, 64, "bf16")
+    ly = make_layer(25, 2048, 64, 256, 512, "bf16", "none")
+    m = synth.cand_to_req_from_counts(np.full(R, C // R)) if C % R == 0 else np.sort(
+        np.random.default_rng(25).integers(0, R, C)).astype(np.int32)
+    note("lcb fused: wait bound %d ns" % wait_ns)
+    ref_r, ref_c = run_lcb(x_r, x_c, ly, m=m)
+    yr, yc = fused_with_wait_bound(wait_ns, lambda: run_lcb(x_r, x_c, ly, m=m))
+    assert same_bits(yr, ref_r)
+    got, want = yc.float().cpu().numpy(), ref_c.float().cpu().numpy()
+    marked = 0
+    for r0 in range(0, C, 256):
+        for c0 in range(0, 512, 256):
+            g, w = got[r0:r0 + 256, c0:c0 + 256], want[r0:r0 + 256, c0:c0 + 256]
+            if np.isnan(g).all():
+                marked += 1
+            else:
+                assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), (r0, c0)
+    print("tiles marked NaN: %d of %d" % (marked, ((C + 255) // 256) * 2))
