@@ -19,15 +19,14 @@
 //    reduction plus one exchange between the two 32-lane halves, and the per-lane partial sums are
 //    combined once at the end. The bf16 weights P^T are the B operand of O^T += V^T P^T; V^T comes
 //    from LDS through ds_read_b64_tr_b16, which transposes 16-bit data across each 16-lane group.
-//  - Softmax in the exp2 domain against a fixed per-query reference m_ref (the max of the first
-//    tile), so O is never rescaled; O / l is exact in real arithmetic for any reference. d = 128:
-//    the scale and the shift are one FMA per score. d = 64, where the softmax VALU work costs
-//    about as many cycles as the MFMAs: the softmax scale times log2(e) is folded into the bf16 Q
-//    fragments once per work tile, and after the first key tile the score MFMAs start from -m_ref
-//    instead of zero, so a score leaves the MFMAs as its exponent (16 more registers, which
-//    d = 128 does not have to spare). A query whose sums leave the fp32 range is redone with its
-//    exact max (a rare second and third pass over its keys); the decision is per query, so a
-//    row's result does not depend on which other rows share its tile.
+//  - Softmax in the exp2 domain with the softmax scale folded into one FMA, against a fixed
+//    per-query reference (the max of the first tile), so O is never rescaled; O / l is exact in
+//    real arithmetic for any reference. The scores stay fp32 products of the bf16 inputs: folding
+//    the scale into bf16 Q fragments instead would save the FMA but round every score by up to
+//    2^-9 of its size, which large keys turn into errors past the accuracy bar. A query whose sums
+//    leave the fp32 range is redone with its exact max (a rare second and third pass over its
+//    keys); the decision is per query, so a row's result does not depend on which other rows
+//    share its tile.
 #include "ikbo_device.h"
 #include "ikbo_launch.h"
 
@@ -140,15 +139,12 @@ __device__ __forceinline__ float block_max(const f32x16 &s) {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Softmax weights of one 32-key block: p = 2^(s * cl2 - m_ref) (EXP 0: s is the raw score),
-// 2^(s - m_ref) (EXP 1: s is scaled already) or 2^s (EXP 2: the MFMAs started from -m_ref); packs
-// the bf16 B operands of the PV MFMAs and adds the packed (rounded) weights to the row sum, so the
-// sum normalises exactly the weights the PV MFMAs use.
-template <int EXP>
-__device__ __forceinline__ void exp_block(f32x16 &s, bf16x8 (&pb)[2], float &l, float cl2, float mref) {
+// p = 2^(s * scale * log2(e) - m_ref) for one 32-key block against a fixed per-query reference;
+// packs the bf16 B operands of the PV MFMAs and adds the packed (rounded) weights to the row sum,
+// so the sum normalises exactly the weights the PV MFMAs use.
+__device__ __forceinline__ void exp_block(f32x16 &s, bf16x8 (&pb)[2], float &l, float cl2, float mneg) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-        s[j] = __builtin_amdgcn_exp2f(EXP == 0 ? __builtin_fmaf(s[j], cl2, -mref) : EXP == 1 ? s[j] - mref : s[j]);
+    for (int j = 0; j < 16; ++j) s[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], cl2, mneg));
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -207,10 +203,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
     const int l32 = lane & 31, half = lane >> 5;
     const int64_t HD = (int64_t)a.H * D;
 
-    constexpr bool FOLD = D == 64;      // scale in Q, -m_ref in the score MFMAs' start value
     const float cl2 = a.scale * 1.4426950408889634f;
 
-    // ---- the lane's query row (one column of S^T); FOLD: scaled by cl2 (bf16, nearest even) ----
+    // ---- the lane's query row (one column of S^T) ----
     const int64_t srow = ti.qb * BM + wave * 32 + l32;
     const bool rvalid = srow < ti.rows;
     // four-wave tiles (short requests): a wave none of whose 32 rows is in the request (the
@@ -227,14 +222,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
         for (int ks = 0; ks < KS; ++ks) {
             uint4 u = rvalid ? *(const uint4 *)(qp + ks * 16) : make_uint4(0, 0, 0, 0);
             qf[ks] = __builtin_bit_cast(bf16x8, u);
-            if constexpr (FOLD) {
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const bf16x2 pr = cvt_bf16x2((float)qf[ks][e] * cl2, (float)qf[ks][e + 1] * cl2);
-                    qf[ks][e] = pr[0];
-                    qf[ks][e + 1] = pr[1];
-                }
-            }
         }
     }
 
@@ -298,13 +285,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
     clear();
 
     bf16x8 pb[NKB][2];      // bf16 weights of the last scored tile (B operands of the PV MFMAs)
-    // FOLD: the accumulator the score MFMAs start from, zero for a pass's first tile, -m_ref after
-    f32x16 cinit;
-    auto set_cinit = [&](float v) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) cinit[j] = FOLD ? v : 0.0f;
-    };
-    set_cinit(0.0f);
+    const f32x16 zero16 = {};
 
     // The score / softmax / PV parts below act on the 32-key blocks kb in [KB0, KB1) of a tile.
     f32x16 sc[NKB];         // scores of the last tile whose MFMAs ran
@@ -328,23 +309,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
             }
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                sc[B0 + b] = mfma_32x32x16_bf16(kf[cur][b], qf[ks], ks == 0 ? cinit : sc[B0 + b]);
+                sc[B0 + b] = mfma_32x32x16_bf16(kf[cur][b], qf[ks], ks == 0 ? zero16 : sc[B0 + b]);
             sched_fence();     // keeps the reads KPD steps ahead, not hoisted further (registers)
         });
     };
     // Softmax weights of tile `it` from sc into pb (MAXONLY: the per-query max only). MASK: the
-    // ragged last tile. FIRST: the pass's first tile; INIT: it also sets m_ref (the main pass; a
-    // whole tile's blocks must be present). FOLD: the first tile was scored from zero and subtracts
-    // m_ref itself, then sets the start value of the later tiles' score MFMAs to -m_ref (the same
-    // in the main pass and a redo, so a query that did not overflow gets the same bits from both).
-    auto softmax = [&](int it, auto KB0, auto KB1, auto mask, auto init, auto first, auto maxonly)
-                       __attribute__((always_inline)) {
+    // ragged last tile. INIT: the main pass's first tile, which sets m_ref (a whole tile's blocks
+    // must be present).
+    auto softmax = [&](int it, auto KB0, auto KB1, auto mask, auto init, auto maxonly) __attribute__((always_inline)) {
         constexpr int B0 = KB0, B1 = KB1;
         constexpr bool MASK = decltype(mask)::value;
         constexpr bool INIT = decltype(init)::value;
-        constexpr bool FIRST = decltype(first)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
-        static_assert(!INIT || (FIRST && B0 == 0 && B1 == NKB), "the reference is the max of a whole first tile");
+        static_assert(!INIT || (B0 == 0 && B1 == NKB), "the reference is the max of a whole tile");
 #pragma unroll
         for (int kb = B0; kb < B1; ++kb)
             if (MASK) mask_block(sc[kb], Lr - it * BN - kb * 32, half);
@@ -352,29 +329,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
 #pragma unroll
             for (int kb = B0; kb < B1; ++kb) mx = fmaxf(mx, block_max(sc[kb]));
         } else {
-            if constexpr (!FOLD) {
-                if constexpr (INIT) {
-                    float m0 = block_max(sc[0]);
+            if constexpr (INIT) {
+                float m0 = block_max(sc[0]);
 #pragma unroll
-                    for (int kb = 1; kb < NKB; ++kb) m0 = fmaxf(m0, block_max(sc[kb]));
-                    mref = m0 * cl2;
-                }
-#pragma unroll
-                for (int kb = B0; kb < B1; ++kb) exp_block<0>(sc[kb], pb[kb], l, cl2, mref);
-            } else if constexpr (FIRST) {
-                if constexpr (INIT) {
-                    float m0 = block_max(sc[0]);
-#pragma unroll
-                    for (int kb = 1; kb < NKB; ++kb) m0 = fmaxf(m0, block_max(sc[kb]));
-                    mref = m0;
-                }
-#pragma unroll
-                for (int kb = B0; kb < B1; ++kb) exp_block<1>(sc[kb], pb[kb], l, cl2, mref);
-                set_cinit(-mref);
-            } else {
-#pragma unroll
-                for (int kb = B0; kb < B1; ++kb) exp_block<2>(sc[kb], pb[kb], l, cl2, mref);
+                for (int kb = 1; kb < NKB; ++kb) m0 = fmaxf(m0, block_max(sc[kb]));
+                mref = m0 * cl2;
             }
+#pragma unroll
+            for (int kb = B0; kb < B1; ++kb) exp_block(sc[kb], pb[kb], l, cl2, -mref);
         }
     };
     auto no_hook = [](auto) {};
@@ -411,22 +373,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
     const std::true_type T;
     const std::false_type F;
     // One whole tile, nothing else in flight (the overflow redo)
-    auto tile = [&](int it, auto S, auto mask, auto first, auto maxonly) __attribute__((always_inline)) {
+    auto tile = [&](int it, auto S, auto mask, auto maxonly) __attribute__((always_inline)) {
         scores(S, K0, KN, no_hook);
-        softmax(it, K0, KN, mask, F, first, maxonly);
+        softmax(it, K0, KN, mask, F, maxonly);
         if constexpr (!decltype(maxonly)::value) pv(S, K0, KN, no_hook);
         wait_vmcnt<0>();
         barrier_lds();
     };
     auto redo_tile = [&](int it, auto maxonly) __attribute__((always_inline)) {
-        const bool last_ragged = ragged && it == ntiles - 1;
-        if (it == 0 && !decltype(maxonly)::value) {
-            if (last_ragged) tile(it, IC<0>{}, T, T, maxonly);
-            else tile(it, IC<0>{}, F, T, maxonly);
-        } else {
-            if (last_ragged) tile(it, IC<0>{}, T, F, maxonly);
-            else tile(it, IC<0>{}, F, F, maxonly);
-        }
+        if (ragged && it == ntiles - 1) tile(it, IC<0>{}, T, maxonly);
+        else tile(it, IC<0>{}, F, maxonly);
     };
 
     // ---- main pass ----
@@ -439,7 +395,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
     constexpr int kInPv = kCopiesPerTile - kInS;
     constexpr int kCPS = (kInS + KS - 1) / KS;
     static_assert((COPYAT == 0 || kInS <= KS) && (kInPv + DB - 1) / DB <= 2, "copy spreading");
-    auto step = [&](int it, auto S, auto mask, auto first) __attribute__((always_inline)) {
+    auto step = [&](int it, auto S, auto mask, auto init) __attribute__((always_inline)) {
         auto copies_s = [&](auto ks) __attribute__((always_inline)) {
             static_for<kCPS>([&](auto u) __attribute__((always_inline)) {
                 constexpr int c = decltype(ks)::value * kCPS + decltype(u)::value;
@@ -452,7 +408,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
         };
         if (active) {
             scores(S, K0, KN, copies_s);
-            softmax(it, K0, KN, mask, first, first, F);
+            softmax(it, K0, KN, mask, init, F);
             pv(S, K0, KN, copies_pv);
         } else {
             // no row of this wave is in the request: only its share of the next tile's copies
@@ -492,16 +448,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
     if (__syncthreads_or(bad)) {
         const float keep = mref;
         clear();
-        set_cinit(0.0f);
         for (int it = 0; it < ntiles; ++it) {
             dma(it * BN, IC<0>{});
             wait_vmcnt<0>();
             barrier_lds();
             redo_tile(it, T);
         }
-        mref = bad ? (FOLD ? mx : mx * cl2) : keep;
+        mref = bad ? mx * cl2 : keep;
         clear();
-        set_cinit(0.0f);
         for (int it = 0; it < ntiles; ++it) {
             dma(it * BN, IC<0>{});
             wait_vmcnt<0>();

@@ -186,19 +186,22 @@ def test_empty_inputs():
     assert got.shape == (0, 1, 1, 64)
 
 
-def test_scores_far_above_the_first_tile_take_the_exact_path():
+@pytest.mark.parametrize("d,hot_value", [(64, 8.0), (128, 8.0), (64, 10.0), (128, 10.0), (64, 12.0), (128, 12.0)])
+def test_scores_far_above_the_first_tile_take_the_exact_path(d, hot_value):
     # Scores in a later key tile far above the first tile's max overflow the fixed-reference sums;
     # those queries are recomputed against their exact max. Other queries of the same work tile
-    # must come out bit for bit as in a run where nothing overflows.
+    # must come out bit for bit as in a run where nothing overflows. The hot key (every element 8)
+    # also makes every query's score against it several times its usual size, which magnifies any
+    # rounding of the queries or scores (a bf16 rounding of the scaled queries fails here).
     counts = [300]
-    L, H, d = 200, 1, 128
+    L, H = 200, 1
     s, q, k, v = make_case(47, counts, [L], H, d, 1, "bf16")
     big_q = q.copy()
     big_k = k.copy()
-    hot = synth.f32_to_bf16_bits(np.full(d, 8.0, np.float32))
+    hot = synth.f32_to_bf16_bits(np.full(d, hot_value, np.float32))
     big_q[5, 0, 0] = hot          # candidate 5's query
-    big_k[150, 0] = hot           # key 150 (third tile): score 8*8*128/sqrt(128) ~ 724 -> 2^1045
-    note("dca exact-path fallback")
+    big_k[150, 0] = hot           # key 150 (third tile): score hot^2 d / sqrt(d), far past 2^128
+    note("dca exact-path fallback d=%d hot=%g" % (d, hot_value))
     got = run_gpu(s, big_q, big_k, v)
     want = oracle.dca(big_q, big_k.reshape(1, L, H, d), v.reshape(1, L, H, d), 1, m=s.cand_to_req)
     assert_parity(down_f64(got), want, "bf16", "fallback")
