@@ -95,8 +95,8 @@ __device__ __forceinline__ void row_source(const DcaArgs &a, const TileInfo &ti,
 // bf16 inputs, D in {64, 128}, MFMA path.
 //
 // Template parameters: NW waves per workgroup, each owning 32 query rows (one column of S^T per
-// lane); NKB 32-key blocks per K/V tile; NBUF LDS stages; KPD / VPD how many k16 steps of K
-// fragments / 32-dim blocks of V^T fragments are read ahead of the MFMAs that use them. Eight
+// lane); NKB 32-key blocks per K/V tile; KPD / VPD how many k16 steps of K fragments / 32-dim
+// blocks of V^T fragments are read ahead of the MFMAs that use them. Two LDS stages. Eight
 // waves put two on every SIMD, so the softmax VALU work of one overlaps the MFMAs of the other in
 // hardware; streaming the fragments from LDS step by step (instead of holding a whole tile) keeps
 // a wave within the 256 registers that two waves per SIMD leave it. One barrier per tile.
@@ -109,7 +109,7 @@ __device__ __forceinline__ void row_source(const DcaArgs &a, const TileInfo &ti,
 // slots, so a lane's source is the (key, column) of its slot. Pad slots, and keys at or past L_r
 // (the buffer range covers the request's rows only), read as zeros without touching memory.
 // Each stage is its own LDS variable and stage indices are compile-time constants (the tile loop
-// is unrolled by NBUF), so reads of one stage are not held back by copies into another.
+// is unrolled by the stage count), so reads of one stage are not held back by copies into another.
 
 // Cross-half combine: v_permlane32_swap exchanges the two 32-lane halves, so the max (or sum) of
 // both results is the value over lanes l and l ^ 32.
@@ -165,7 +165,7 @@ __device__ __forceinline__ void exp_block(f32x16 &s, bf16x8 (&pb)[2], float &l, 
 template <int D, int NW>
 constexpr int dca_min_waves() { return NW == 4 && D == 64 ? 3 : NW >= 4 ? 2 : 1; }
 
-template <int D, int NW, int NKB, int NBUF, int KPD, int VPD, int COPYAT>
+template <int D, int NW, int NKB, int KPD, int VPD>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min_waves<D, NW>(), 8))) void dca_bf16_kernel(DcaArgs a) {
     constexpr int BN = NKB * 32;                       // keys per tile
     constexpr int BM = NW * 32;                        // stacked query rows per workgroup
@@ -176,23 +176,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
     constexpr int kInstrK = (BN * KSR + 63) / 64, kInstrV = (BN * VSR + 63) / 64;
     constexpr int kPassK = (kInstrK + NW - 1) / NW, kPassV = (kInstrV + NW - 1) / NW;
     constexpr int kCopiesPerTile = kPassK + kPassV;     // at most, per wave
-    static_assert(NBUF == 2, "copies of the next tile are waited for in full at each barrier");
-    static_assert(NBUF == 2 || NBUF == 3, "two or three LDS stages");
-    static_assert((NBUF - 2) * kCopiesPerTile < 64, "vmcnt range");
+    constexpr int NBUF = 2;     // LDS stages: the copies of the next tile are waited for at each barrier
     constexpr int KS = D / 16, DB = D / 32;
     constexpr uint32_t kOutOfRange = 0x80000000u;
 
-    __shared__ uint4 k_s0[kInstrK * 64], k_s1[kInstrK * 64], k_s2[NBUF > 2 ? kInstrK * 64 : 1];
-    __shared__ uint4 v_s0[kInstrV * 64], v_s1[kInstrV * 64], v_s2[NBUF > 2 ? kInstrV * 64 : 1];
+    __shared__ uint4 k_s0[kInstrK * 64], k_s1[kInstrK * 64];
+    __shared__ uint4 v_s0[kInstrV * 64], v_s1[kInstrV * 64];
     auto k_lds = [&](auto S) __attribute__((always_inline)) -> uint4 * {
         if constexpr (decltype(S)::value == 0) return k_s0;
-        else if constexpr (decltype(S)::value == 1) return k_s1;
-        else return k_s2;
+        else return k_s1;
     };
     auto v_lds = [&](auto S) __attribute__((always_inline)) -> uint4 * {
         if constexpr (decltype(S)::value == 0) return v_s0;
-        else if constexpr (decltype(S)::value == 1) return v_s1;
-        else return v_s2;
+        else return v_s1;
     };
 
     TileInfo ti;
@@ -388,32 +384,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
     // ---- main pass ----
     // The copies of tile it + 1 go out one per k16 step of tile it's scores, so the eight waves
     // do not queue all their copies at once right after the barrier; the copy unit is fed while
-    // the MFMAs run. Each barrier waits for the whole next tile.
-    // COPYAT 0: all copies in the k16 steps of the scores (kCPS per step: one with eight waves,
-    // more when fewer waves share a tile's copies); 1: in the 32-dim steps of PV; 2: split
-    constexpr int kInS = COPYAT == 0 ? kCopiesPerTile : COPYAT == 1 ? 0 : (kCopiesPerTile + 1) / 2;
-    constexpr int kInPv = kCopiesPerTile - kInS;
-    constexpr int kCPS = (kInS + KS - 1) / KS;
-    static_assert((COPYAT == 0 || kInS <= KS) && (kInPv + DB - 1) / DB <= 2, "copy spreading");
+    // the MFMAs run (kCPS copies per step: one with eight waves, more when fewer waves share a
+    // tile's copies). Each barrier waits for the whole next tile.
+    constexpr int kCPS = (kCopiesPerTile + KS - 1) / KS;
     auto step = [&](int it, auto S, auto mask, auto init) __attribute__((always_inline)) {
         auto copies_s = [&](auto ks) __attribute__((always_inline)) {
             static_for<kCPS>([&](auto u) __attribute__((always_inline)) {
                 constexpr int c = decltype(ks)::value * kCPS + decltype(u)::value;
-                if constexpr (c < kInS) copy(c, (it + 1) * BN, IC<(S + 1) % NBUF>{});
+                if constexpr (c < kCopiesPerTile) copy(c, (it + 1) * BN, IC<(S + 1) % NBUF>{});
             });
-        };
-        auto copies_pv = [&](auto db) __attribute__((always_inline)) {
-            if constexpr (db < kInPv) copy(kInS + db, (it + 1) * BN, IC<(S + 1) % NBUF>{});
-            if constexpr (db + DB < kInPv) copy(kInS + DB + db, (it + 1) * BN, IC<(S + 1) % NBUF>{});
         };
         if (active) {
             scores(S, K0, KN, copies_s);
             softmax(it, K0, KN, mask, init, F);
-            pv(S, K0, KN, copies_pv);
+            pv(S, K0, KN, no_hook);
         } else {
             // no row of this wave is in the request: only its share of the next tile's copies
             static_for<KS>(copies_s);
-            static_for<DB>(copies_pv);
         }
         wait_vmcnt<0>();     // tile it + 1 landed
         barrier_lds();
@@ -518,14 +505,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dca_min
 }
 
 // The configurations the library launches, per head dim: 8 waves x 32 query rows, 64-key tiles,
-// two LDS stages, K reads two k16 steps ahead (mode 0); for requests with a few hundred stacked
-// query rows, 4 waves of 32 rows, two workgroups per CU (mode 2: a request's last work tile is
-// on average half as empty); and for requests with very few rows (the request-side attention has
-// q_len rows per request), one wave of 32 rows (mode 1). Each row's arithmetic is the same in all
-// three, so are the results.
+// K and V^T fragments read one step ahead of their MFMAs (mode 0); for requests with a few hundred
+// stacked query rows, 4 waves of 32 rows, two or three workgroups per CU (mode 2: a request's last
+// work tile is on average half as empty); and for requests with very few rows (the request-side
+// attention has q_len rows per request), one wave of 32 rows (mode 1). Each row's arithmetic is
+// the same in all three, so are the results.
 template <int D, int MODE = 0>
 struct DcaBf16Config {
-    static constexpr int NW = MODE == 1 ? 1 : MODE == 2 ? 4 : 8, NKB = 2, NBUF = 2, KPD = 1, VPD = 1, COPYAT = 0;
+    static constexpr int NW = MODE == 1 ? 1 : MODE == 2 ? 4 : 8, NKB = 2, KPD = 1, VPD = 1;
     static constexpr int BM = NW * 32;
 };
 
@@ -635,7 +622,7 @@ hipError_t launch_dca(const DcaArgs &a, hipStream_t s) {
 #define IKBO_DCA_LAUNCH(DD, SM)                                                                                         \
     do {                                                                                                               \
         using C = DcaBf16Config<DD, SM>;                                                                               \
-        hipLaunchKernelGGL((dca_bf16_kernel<DD, C::NW, C::NKB, C::NBUF, C::KPD, C::VPD, C::COPYAT>), dim3((unsigned)grid), \
+        hipLaunchKernelGGL((dca_bf16_kernel<DD, C::NW, C::NKB, C::KPD, C::VPD>), dim3((unsigned)grid),                     \
                            dim3(C::NW * 64), 0, s, a);                                                                 \
     } while (0)
         if (a.D == 128) {
