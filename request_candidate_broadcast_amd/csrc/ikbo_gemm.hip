@@ -29,6 +29,7 @@ namespace {
 // in two LDS stages
 constexpr int kWGM = 4, kWGN = 2, kTM = 64, kTN = 128;
 constexpr int BM = kWGM * kTM, BN = kWGN * kTN, BK = 64;
+constexpr int kGemmGroupM = 8;     // row blocks per tile group of the one-tile-per-workgroup GEMM
 constexpr int kGemmThreads = kWGM * kWGN * 64;
 
 __device__ __forceinline__ float apply_act(int act, float x) { return act == 1 ? gelu_exact(x) : x; }
@@ -657,10 +658,23 @@ __global__ __launch_bounds__(WGM *WGN * 64) void gemm_bf16_t(GemmArgs a, int32_t
     const int64_t total = (int64_t)tiles_m * tiles_n * a.splits;
     int64_t t = xcd_tile(blockIdx.x, total);
     if (t < 0) return;
-    const int nt = (int)(t % tiles_n);
-    t /= tiles_n;
-    const int mt = (int)(t % tiles_m);
-    const int sp = (int)(t / tiles_m);
+    int nt, mt, sp;
+    if constexpr (!PARTIAL) {
+        // groups of kGemmGroupM row blocks: within a group the column tile changes slowest, so
+        // consecutive tiles share one weight tile and the column tiles of a row block (which
+        // share its activation tile) are kGemmGroupM tiles apart, still running together on
+        // the XCD
+        const int64_t gsz = (int64_t)kGemmGroupM * tiles_n, g = t / gsz, r = t % gsz;
+        const int64_t rows = min((int64_t)kGemmGroupM, (int64_t)tiles_m - g * kGemmGroupM);
+        nt = (int)(r / rows);
+        mt = (int)(g * kGemmGroupM + r % rows);
+        sp = 0;
+    } else {
+        nt = (int)(t % tiles_n);
+        t /= tiles_n;
+        mt = (int)(t % tiles_m);
+        sp = (int)(t / tiles_m);
+    }
     gemm_tile<WGM, WGN, TM, TN, TBK, NBUF, DMA, PARTIAL, false, STG>(a, mt, nt, sp, k_per_split, sx, sw, [] {});
 }
 
