@@ -32,6 +32,20 @@ EXTRA_WORKLOADS = ("dca_fixed", "dca_ragged", "lcb")
 # requests, candidates per request, n_r, n_c (input embeddings), d, k_r, k_c (output embeddings)
 LCBE_SHAPE = (128, 2048, 32, 32, 64, 32, 32)
 
+# The kernel figures the pages print, as context beside the measured line (not a target: their
+# hardware, precision and shapes differ and are not all stated). ROCS: Request-Oriented Compute
+# Sharing, Sec. 5.2.5 (Tables 4 and 5); Request-Level Sharing Cuts Recommendation Inference Cost,
+# "Technical Approach".
+PAGES_CONTEXT = {
+    "hardware": "Hopper-class GPU (the kernels use WGMMA and TMA; the tables name no GPU)",
+    "shapes_and_precision": "not stated for these tables",
+    "ikbo_lcb_ms": {"original": 1.944, "after_decomposition": 1.389, "after_alignment": 0.798,
+                    "after_broadcast_fusion": 0.580, "after_pipelining_and_fusion": 0.482},
+    "ikbo_dca": {"tflops": 594, "ms": 0.230, "gbs": 681},
+    "fa_baselines_with_explicit_broadcast": {"tlx_fa3_tflops": 245, "tlx_fa3_ms": 1.473,
+                                              "cutedsl_fa_tflops": 250, "cutedsl_fa_ms": 1.462},
+}
+
 
 def stack_layer2(np, synth, s):
     """The second interaction layer of the stack workload: its query generator reads the first
@@ -251,6 +265,7 @@ def main():
             line["ikbo_lcb_ms"] = extra["lcb"]["parts"]["lcb"]["ms_avg"]
     if alt:
         line["alternate_forms"] = alt
+    line["pages_context"] = PAGES_CONTEXT
     if cold:
         line["cold_l2"] = {k: ({kk: round(vv, 4) for kk, vv in d.items()} if isinstance(d, dict) else d)
                            for k, d in cold.items()}
