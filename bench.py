@@ -584,8 +584,9 @@ def setup(workload, args, np, torch, ikbo, synth, dev, stream, up):
 
 def measure_ceilings(torch, ikbo, stream):
     """What kernels of this part reach on their own (libikbo_probe.so), beside the published peaks:
-    dense bf16 MFMA from register operands, HBM copy and read streams, v_exp_f32 evaluations.
-    Median of 5 timed launches after one warm-up each."""
+    dense bf16 MFMA from register operands, HBM copy and read streams, v_exp_f32 evaluations, LDS
+    reads (ds_read_b128, and ds_read_b64_tr_b16 over 320-byte rows, the transposed V^T reads of the
+    d = 128 attention kernel). Median of 5 timed launches after one warm-up each."""
     dev = torch.device("cuda:0")
 
     def timed(kind, buf, iters, blocks):
@@ -609,6 +610,10 @@ def measure_ceilings(torch, ikbo, stream):
     iters, blocks = 8000, 2048
     sec = timed(ikbo.IKBO_PROBE_EXP2, small, iters, blocks)
     out["exp2_per_s"] = float("%.4g" % (blocks * 256 * iters * 8 / sec))
+    iters, blocks = 2000, 1024                 # four blocks of 4 waves and 32 KiB of LDS per CU
+    for kind, key, per in ((ikbo.IKBO_PROBE_LDS_B128, "lds_read_b128_tbs", 1024),
+                           (ikbo.IKBO_PROBE_LDS_TR16, "lds_read_tr16_tbs", 512)):
+        out[key] = round(blocks * 4 * iters * 16 * per / timed(kind, small, iters, blocks) / 1e12, 1)
     big = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     big.zero_()
     # 1 GiB read + 1 GiB written; the best of three grid sizes (one to four rounds of resident waves)

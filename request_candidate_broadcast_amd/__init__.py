@@ -66,6 +66,7 @@ _lib = None
 
 PROBE_PATH = os.path.join(PKG_DIR, "libikbo_probe.so")
 IKBO_PROBE_MFMA_BF16, IKBO_PROBE_EXP2, IKBO_PROBE_COPY, IKBO_PROBE_READ = 0, 1, 2, 3
+IKBO_PROBE_LDS_B128, IKBO_PROBE_LDS_TR16 = 4, 5
 _probe = None
 
 

@@ -1,5 +1,6 @@
 // Ceiling probes for the roofline: the rates a kernel of this part can reach on its own, measured
-// beside the published peaks (bf16 dense MFMA, HBM, and the transcendental unit the softmax uses).
+// beside the published peaks (bf16 dense MFMA, HBM, the transcendental unit the softmax uses, and
+// LDS reads).
 // Each probe is a bounded loop over registers or a grid-stride pass over a buffer; none depends
 // on the method. The caller times the launch (events on the stream) and divides the work below.
 #include "ikbo_probe.h"
@@ -95,6 +96,46 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const uint4 *src, int64
     out[t] = x;
 }
 
+// LDS reads: each block fills 32 KiB of LDS with one runtime value, then every wave issues 16 reads
+// per round, `iters` rounds, at addresses that move with the round (so no read leaves the loop).
+// TR = false: ds_read_b128, lane l at 16 l of a 1 KiB block (1 KiB per wave instruction).
+// TR = true: ds_read_b64_tr_b16 (512 B per wave instruction) over rows of 320 bytes (128 16-bit
+// elements plus 32 of padding), each 16-lane group reading 4 rows by 64 bytes, in pairs 8 rows
+// apart. Every read returns copies of the fill value, so the xor of each round's reads is 0 and
+// every thread writes 0.
+typedef short probe_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) probe_i16x4 probe_lds_i16x4;
+
+template <bool TR>
+__global__ __launch_bounds__(256) void probe_lds_kernel(uint32_t *out, int64_t iters) {
+    __shared__ uint4 buf[2048];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t h = (uint32_t)(iters * 2654435761LL) & 0xffffu;
+    const uint32_t w = h | (h << 16);
+    for (int i = tid; i < 2048; i += 256) buf[i] = make_uint4(w, w, w, w);
+    __syncthreads();
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int tr_base = (4 * (g16 >> 1) + (s16 >> 2)) * 320 + ((g16 & 1) * 16 + 4 * (s16 & 3)) * 2;
+    uint32_t acc = 0;
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if constexpr (TR) {
+                const int off = (int)((it + k) & 1) * 8192 + tr_base + ((k >> 2) & 1) * 32 * 320 + (k & 3) * 64 +
+                                (k >> 3) * 8 * 320;
+                const probe_i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (probe_lds_i16x4 *)((__attribute__((address_space(3))) char *)buf + off));
+                acc ^= (uint32_t)(uint16_t)r[0] ^ (uint32_t)(uint16_t)r[1] ^ (uint32_t)(uint16_t)r[2] ^
+                       (uint32_t)(uint16_t)r[3];
+            } else {
+                const uint4 v = buf[(int)((it * 16 + k + wave * 5) & 31) * 64 + lane];
+                acc ^= v.x ^ v.y ^ v.z ^ v.w;
+            }
+        }
+    }
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,6 +169,14 @@ int ikbo_probe_launch(int32_t kind, void *buf, size_t bytes, int64_t iters, int6
                                (uint32_t *)((char *)buf + (size_t)n16 * 16));
             break;
         }
+        case IKBO_PROBE_LDS_B128:
+            if (bytes < per_thread_out) return 1;
+            hipLaunchKernelGGL(probe_lds_kernel<false>, grid, block, 0, s, (uint32_t *)buf, iters);
+            break;
+        case IKBO_PROBE_LDS_TR16:
+            if (bytes < per_thread_out) return 1;
+            hipLaunchKernelGGL(probe_lds_kernel<true>, grid, block, 0, s, (uint32_t *)buf, iters);
+            break;
         default:
             return 1;
     }

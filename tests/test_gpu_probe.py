@@ -35,3 +35,10 @@ def test_probes_run_and_write_their_outputs():
     torch.cuda.synchronize()
     # the last blocks * 256 words hold one xor of each thread's reads: ones xor'd in fours -> 0
     assert torch.count_nonzero(src[-blocks * 256:]).item() == 0
+    for kind, name in ((ikbo.IKBO_PROBE_LDS_B128, "lds b128"), (ikbo.IKBO_PROBE_LDS_TR16, "lds tr16")):
+        note("probe " + name)
+        words = torch.full((blocks * 256,), -1, dtype=torch.int32, device=dev)
+        ikbo.ikbo_probe_launch(kind, words, 10, blocks)
+        torch.cuda.synchronize()
+        # every read returns copies of the fill value; an even number of them xor to 0
+        assert torch.count_nonzero(words).item() == 0
