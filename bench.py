@@ -607,6 +607,9 @@ def measure_ceilings(torch, ikbo, stream):
         sec = timed(ikbo.IKBO_PROBE_MFMA_BF16, small, iters, blocks)
         best = max(best, blocks * 4 * iters * 4 * 32768.0 / sec / 1e12)
     out["mfma_bf16_tflops"] = round(best, 1)
+    # the same four chains with one wave per SIMD (256 blocks of 4 waves): what one wave can issue
+    sec = timed(ikbo.IKBO_PROBE_MFMA_BF16, small, 20000, 256)
+    out["mfma_bf16_tflops_one_wave_per_simd"] = round(256 * 4 * 20000 * 4 * 32768.0 / sec / 1e12, 1)
     iters, blocks = 8000, 2048
     sec = timed(ikbo.IKBO_PROBE_EXP2, small, iters, blocks)
     out["exp2_per_s"] = float("%.4g" % (blocks * 256 * iters * 8 / sec))
