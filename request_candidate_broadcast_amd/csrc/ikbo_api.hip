@@ -407,7 +407,6 @@ static int dca_run(const void *q, int64_t C, int32_t q_len, const void *k, const
     if (!in_f32 && (q_cs % 8 != 0 || o_cs % 8 != 0))
         return fail(IKBO_MISALIGNED, "candidate row strides must be multiples of 8 elements");
     const int ob = (int)esize(out_dtype);
-    // few stacked query rows per request (at most 32 on average): one-wave, 32-row work tiles
     // work tile by the average stacked query rows per request: at most 32 one wave, at most 1024
     // four waves (128 rows), else eight (256 rows); a request's last tile is partly empty, and
     // smaller tiles waste fewer rows where requests are short
